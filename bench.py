@@ -1,0 +1,253 @@
+"""Benchmark of the FP8 top-k sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, inputs resident
+in HBM: fp8_quantize(Q), fp8_quantize(idx_q), indexer_topk, sparse_attn_fwd.
+Default workload: 8192-token causal GQA block-sparse prefill (16 q / 2 kv
+heads, d 128, page 128, 4 index heads, top-64 blocks).
+
+Prints ONE JSON line.  ``value`` = algorithmic attention TFLOP/s over the whole
+step; ``roofline`` describes the dominant kernel (sparse attention), timed with
+HIP events on the stream it runs on; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+PAGE = 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def block_attention_flops(ids: np.ndarray, pos: np.ndarray, hq: int, hidx: int, d_qk: int, d_v: int) -> int:
+    """Exact algorithmic flops: 2 (d_qk + d_v) per (query head, visible selected key)."""
+    valid = ids >= 0
+    n = np.clip(pos[None, :, None] + 1 - PAGE * ids.astype(np.int64), 0, PAGE)
+    keys = int(np.where(valid, n, 0).sum())
+    return keys * (hq // hidx) * 2 * (d_qk + d_v)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_top_sparse_amd as fts
+    import workloads as W
+
+    fts.load()
+    torch.cuda.set_device(0)
+    wl = W.workload(args.workload)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    block = isinstance(wl, W.BlockWorkload)
+    if block:
+        Q = bf(wl.q_bf16)
+        IQ = bf(wl.idx_q_bf16)
+        KC, VC, IK = d(wl.k_cache8), d(wl.v_cache8), d(wl.idx_k8)
+        BT, CU, SL = d(wl.block_table), d(wl.cu_seqlens_q), d(wl.seq_lens)
+        T, Hq, D = wl.q_bf16.shape
+        Hidx = wl.idx_q_bf16.shape[1]
+        Hkv = wl.k_cache8.shape[1]
+        q8 = torch.empty((T, Hq, D), dtype=torch.uint8, device="cuda")
+        iq8 = torch.empty((T, Hidx, D), dtype=torch.uint8, device="cuda")
+        ids = torch.empty((Hidx, T, wl.topk), dtype=torch.int32, device="cuda")
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+        ml = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+        lib = fts.load()
+        iws = torch.empty(max(1, lib.indexer_topk_workspace_size(T, Hidx, wl.block_table.shape[1])),
+                          dtype=torch.uint8, device="cuda")
+        aws_n = lib.sparse_attn_workspace_size(1, wl.block_table.shape[0], T, wl.max_q_len, Hq, Hkv, Hidx, D,
+                                               wl.topk, wl.block_table.shape[1])
+        aws = torch.empty(max(1, aws_n), dtype=torch.uint8, device="cuda")
+    else:
+        Q = bf(wl.q_bf16)
+        KV, IDX = d(wl.kv8), d(wl.indices)
+        SINK = None if wl.sink is None else d(wl.sink)
+        T, Hq, Dqk = wl.q_bf16.shape
+        q8 = torch.empty((T, Hq, Dqk), dtype=torch.uint8, device="cuda")
+        out = torch.empty((T, Hq, wl.d_v), dtype=torch.bfloat16, device="cuda")
+        ml = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+        lib = fts.load()
+        aws_n = lib.sparse_attn_workspace_size(0, 0, T, 0, Hq, 1, 1, wl.d_v, wl.indices.shape[1], 0)
+        aws = torch.empty(max(1, aws_n), dtype=torch.uint8, device="cuda")
+
+    kinds = ("quant", "index", "attn") if block else ("quant", "attn")
+
+    def new_events():
+        return {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in kinds}
+
+    def step(ev=None):
+        def rec(k, i):
+            if ev is not None:
+                ev[k][i].record()
+        rec("quant", 0)
+        fts.fp8_quantize(Q, wl.q_scale, out=q8)
+        if block:
+            fts.fp8_quantize(IQ, wl.idx_q_scale, out=iq8)
+        rec("quant", 1)
+        if block:
+            rec("index", 0)
+            fts.indexer_topk(iq8, IK, BT, CU, SL, max_q_len=wl.max_q_len, sm_scale=wl.idx_sm_scale,
+                             topk=wl.topk, idx_q_scale=wl.idx_q_scale, idx_k_scale=wl.idx_k_scale, out=ids,
+                             workspace=iws)
+            rec("index", 1)
+            rec("attn", 0)
+            fts.sparse_attn_fwd(q8, KC, ids, v=VC, sm_scale=wl.sm_scale, mode="block", block_table=BT,
+                                cu_seqlens_q=CU, seq_lens=SL, max_q_len=wl.max_q_len, q_scale=wl.q_scale,
+                                k_scale=wl.k_scale, v_scale=wl.v_scale, out=out, max_logits=ml, lse=lse,
+                                workspace=aws)
+            rec("attn", 1)
+        else:
+            rec("attn", 0)
+            fts.sparse_attn_fwd(q8, KV, IDX, sm_scale=wl.sm_scale, mode="token", d_v=wl.d_v,
+                                q_scale=wl.q_scale, k_scale=wl.k_scale, v_scale=wl.v_scale, attn_sink=SINK,
+                                out=out, max_logits=ml, lse=lse, workspace=aws)
+            rec("attn", 1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # algorithmic work, counted from the path's own selections
+    if block:
+        from oracle.indexer import positions   # host-side position arithmetic for the work count
+        _, pos = positions(wl.cu_seqlens_q, wl.seq_lens)
+        ids_h = ids.cpu().numpy()
+        flops = block_attention_flops(ids_h, pos, Hq, Hidx, D, D)
+        quant_bytes = 3 * (wl.q_bf16.size + wl.idx_q_bf16.size)
+        # indexer bytes: ids written; when some row needs scoring, also the index
+        # query and every index key of the sequence read once
+        nb = pos // PAGE + 1
+        index_bytes = ids_h.size * 4
+        if (nb > wl.topk).any():
+            index_bytes += wl.idx_q_bf16.size + int(wl.seq_lens.sum()) * 128
+    else:
+        idx = wl.indices
+        n_valid = int(((idx >= 0) & (idx < wl.kv8.shape[0])).sum())
+        flops = n_valid * Hq * 2 * (Dqk + wl.d_v)
+        quant_bytes = 3 * wl.q_bf16.size
+        index_bytes = 0
+
+    # timed region: exactly K steps, per-kernel HIP events recorded on the launch stream
+    evs = [new_events() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in kinds}
+    ms.setdefault("index", None)
+
+    ms_step = total_ms / args.steps
+    attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": "fp8 sparse-attn prefill TFLOP/s (% fp8 MFMA peak); indexer top-k GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (QK) / bf16 (PV)",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": int(T), "q_heads": int(Hq),
+                   "attention_gflop_per_step": round(flops / 1e9, 3),
+                   "parallelism": "single GPU"},
+        "kernels_ms": {k: (round(v, 4) if v is not None else None) for k, v in ms.items()},
+        "attention_tflops": round(attn_tflops, 3),
+        "attention_frac_fp8_peak": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
+        "quantize_GBps": round(quant_bytes / (ms["quant"] * 1e-3) / 1e9, 1),
+        "indexer_topk_GBps": (round(index_bytes / (ms["index"] * 1e-3) / 1e9, 1)
+                              if block and ms["index"] else None),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, block)
+    print(json.dumps(result))
+
+
+def cpu_baseline(wl, block: bool) -> dict:
+    """The CPU oracle (float64, numpy) on a bounded sample of the same workload."""
+    import workloads as W  # noqa: F401
+    from oracle import attention as OA
+    from oracle import indexer as OI
+    from oracle import quantize as OQ
+
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    T = wl.q_bf16.shape[0]
+    n = 6 if block else 4
+    toks = np.sort(rng.choice(T, n, replace=False))
+    t0 = time.perf_counter()
+    q8 = OQ.quantize(wl.q_bf16[toks], OQ.BF16, wl.q_scale)
+    if block:
+        iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
+        ids = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                              sm_scale=wl.idx_sm_scale, idx_q_scale=wl.idx_q_scale,
+                              idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=toks)
+        full_q8 = np.zeros(wl.q_bf16.shape, np.uint8)
+        full_q8[toks] = q8
+        full_ids = np.full((ids.shape[0], T, wl.topk), -1, np.int32)
+        full_ids[:, toks] = ids
+        OA.sparse_attn_block(full_q8, wl.k_cache8, wl.v_cache8, full_ids, wl.block_table, wl.cu_seqlens_q,
+                             wl.seq_lens, sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale, tokens=toks)
+        _, pos = OI.positions(wl.cu_seqlens_q, wl.seq_lens)
+        flops = block_attention_flops(ids, pos[toks], wl.q_bf16.shape[1], ids.shape[0], 128, 128)
+    else:
+        full_q8 = np.zeros(wl.q_bf16.shape, np.uint8)
+        full_q8[toks] = q8
+        OA.sparse_attn_token(full_q8, wl.kv8, wl.indices, sm_scale=wl.sm_scale, d_v=wl.d_v, q_scale=wl.q_scale,
+                             k_scale=wl.k_scale, v_scale=wl.v_scale, attn_sink=wl.sink, tokens=toks)
+        flops = int((wl.indices[toks] >= 0).sum()) * wl.q_bf16.shape[1] * 2 * (576 + wl.d_v)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} query tokens of {wl.name} through quantize, indexer and attention "
+                      f"(float64 numpy, {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

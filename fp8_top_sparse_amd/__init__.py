@@ -1,0 +1,277 @@
+"""Python binding of libfp8ts.so: FP8-e4m3 top-k sparse attention on MI355X.
+
+Argument marshalling only.  Every step runs in the HIP library; torch is used
+for device memory and the current stream.  If the library cannot be loaded
+the calls raise: there is no CPU fallback.
+
+Functions (same names as the C ABI in ``include/fp8ts.h``):
+
+* :func:`fp8_quantize`     bf16/fp16 tensor -> e4m3 bytes (per-tensor scale).
+* :func:`indexer_topk`     lightning-indexer ascending top-k block ids.
+* :func:`sparse_attn_fwd`  sparse attention forward (token or block mode).
+
+fp8 tensors are exchanged as ``torch.uint8`` holding e4m3fn bytes
+(``torch.float8_e4m3fn`` inputs are accepted and viewed as bytes).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8ts.so")
+
+BF16, FP16 = 0, 1
+TOKEN_MODE, BLOCK_MODE = 0, 1
+_ST_OK, _ST_EINVAL, _ST_EUNSUP, _ST_EHIP = 0, 1, 2, 3
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_fp = ctypes.POINTER(ctypes.c_float)
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "fp8ts_last_error": ([], ctypes.c_char_p),
+    "fp8ts_abi_version": ([], ctypes.c_int),
+    "fp8_quantize": ([_vp, _i32, _i64, _i64, _i64, _vp, _i64, _fp, _vp], ctypes.c_int),
+    "indexer_topk_workspace_size": ([_i32, _i32, _i32], _sz),
+    "indexer_topk": ([_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                      _fp, _fp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_workspace_size": ([_i32] * 10, _sz),
+    "sparse_attn_fwd": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp, _vp,
+                         _sz, _vp], ctypes.c_int),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+
+class Fp8tsError(RuntimeError):
+    """A HIP runtime failure reported by the library."""
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8ts.so (once).  Raises if it is missing: no fallback exists."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m fp8_top_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status == _ST_OK:
+        return
+    msg = _lib.fp8ts_last_error().decode()
+    if status in (_ST_EINVAL, _ST_EUNSUP):
+        raise ValueError(msg)
+    raise Fp8tsError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _scale(s: Optional[float]):
+    return None if s is None else ctypes.byref(ctypes.c_float(float(s)))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bytes(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    raise ValueError(f"expected e4m3 bytes (uint8 or float8_e4m3fn), got {t.dtype}")
+
+
+def _i32t(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def flatten_to_2d(x: torch.Tensor):
+    """(rows, cols, row_stride) of a tensor whose leading dims flatten onto one stride.
+
+    Raises ValueError when the last dim is not contiguous or the leading dims
+    cannot be expressed with a single row stride.
+    """
+    if x.dim() == 0:
+        return 1, 1, 1
+    if x.numel() == 0:
+        return 0, x.shape[-1], x.shape[-1]
+    if x.stride(-1) != 1:
+        raise ValueError(f"last dim must be contiguous (stride {x.stride(-1)})")
+    cols = x.shape[-1]
+    if x.dim() == 1:
+        return 1, cols, cols
+    rows = x.numel() // cols if cols else 0
+    row_stride = x.stride(-2)
+    for d in range(x.dim() - 2):
+        expected = x.shape[d + 1] * x.stride(d + 1)
+        if x.shape[d] > 1 and x.stride(d) != expected:
+            raise ValueError(f"cannot flatten dim {d}: stride {x.stride(d)} != {expected}")
+    return rows, cols, row_stride
+
+
+def fp8_quantize(x: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """e4m3 bytes of ``x / scale`` (``scale=None``: no scaling), same shape as x."""
+    lib = load()
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float16:
+        dt = FP16
+    else:
+        raise ValueError(f"x must be bf16 or fp16, got {x.dtype}")
+    rows, cols, xs = flatten_to_2d(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    out = _bytes(out)
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError(f"out shape {tuple(out.shape)} != x shape {tuple(x.shape)}")
+    orows, _, os_ = flatten_to_2d(out)
+    if orows != rows:
+        raise ValueError("out does not flatten like x")
+    _check(lib.fp8_quantize(_ptr(x), dt, rows, cols, xs, _ptr(out), os_, _scale(scale), _stream(stream)))
+    return out
+
+
+def indexer_topk(idx_q: torch.Tensor, idx_k: torch.Tensor, block_table: torch.Tensor,
+                 cu_seqlens_q: torch.Tensor, seq_lens: torch.Tensor, *, max_q_len: int, sm_scale: float,
+                 topk: int, idx_q_scale: Optional[float] = None, idx_k_scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Top-k block ids ``[H, total_q, topk]`` int32, strictly ascending, -1 padded.
+
+    idx_q ``[total_q, H, 128]`` e4m3; idx_k ``[num_pages, 128, 128]`` e4m3;
+    block_table ``[batch, max_blocks]``; cu_seqlens_q ``[batch+1]``; seq_lens ``[batch]``.
+    """
+    lib = load()
+    q = _bytes(idx_q)
+    k = _bytes(idx_k)
+    if q.dim() != 3 or k.dim() != 3 or not q.is_contiguous() or not k.is_contiguous():
+        raise ValueError("idx_q must be [T, H, D] and idx_k [pages, page, D], contiguous")
+    T, H, D = q.shape
+    pages, page, Dk = k.shape
+    if Dk != D:
+        raise ValueError(f"idx_k head dim {Dk} != idx_q head dim {D}")
+    bt = _i32t(block_table, "block_table")
+    cu = _i32t(cu_seqlens_q, "cu_seqlens_q")
+    sl = _i32t(seq_lens, "seq_lens")
+    B, max_blocks = bt.shape
+    if out is None:
+        out = torch.empty((H, T, topk), dtype=torch.int32, device=q.device)
+    need = lib.indexer_topk_workspace_size(T, H, max_blocks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.indexer_topk(_ptr(q), _ptr(k), pages, _ptr(bt), max_blocks, _ptr(cu), _ptr(sl), B, T,
+                            int(max_q_len), H, D, page, float(sm_scale), _scale(idx_q_scale),
+                            _scale(idx_k_scale), int(topk), _ptr(out), _ptr(workspace), wsz,
+                            _stream(stream)))
+    return out
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, sm_scale: float,
+                    mode: str = "token", v: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
+                    topk_length: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                    cu_seqlens_q: Optional[torch.Tensor] = None, seq_lens: Optional[torch.Tensor] = None,
+                    max_q_len: int = 0, q_scale: Optional[float] = None, k_scale: Optional[float] = None,
+                    v_scale: Optional[float] = None, attn_sink: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Sparse attention forward.  Returns ``(out bf16, max_logits fp32, lse fp32)``.
+
+    mode "token": q ``[T, Hq, 576]``, k ``[S, 576]`` (V = first d_v=512 columns
+    unless ``v [S, 512]`` is given), indices ``[T, topk]`` token ids.
+    mode "block": q ``[T, Hq, 128]``, k/v ``[pages, Hkv, 128, 128]`` paged caches,
+    indices ``[Hidx, T, topk]`` block ids, plus block_table / cu_seqlens_q /
+    seq_lens / max_q_len as for :func:`indexer_topk`.
+    """
+    lib = load()
+    qb = _bytes(q)
+    kb = _bytes(k)
+    vb = None if v is None else _bytes(v)
+    if qb.dim() != 3 or not qb.is_contiguous():
+        raise ValueError("q must be a contiguous [T, Hq, Dqk] tensor")
+    T, Hq, Dqk = qb.shape
+    idx = _i32t(indices, "indices")
+    for t in (kb, vb):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("k / v must be contiguous")
+    if mode == "token":
+        m = TOKEN_MODE
+        if kb.dim() != 2:
+            raise ValueError("token mode: k must be [S, Dqk]")
+        num_kv, Hkv, Hidx = kb.shape[0], 1, 1
+        Dv = d_v if d_v is not None else (vb.shape[-1] if vb is not None else 512)
+        if idx.dim() != 2 or idx.shape[0] != T:
+            raise ValueError("token mode: indices must be [T, topk]")
+        topk = idx.shape[1]
+        page, max_blocks, B = 0, 0, 0
+        bt = cu = sl = None
+    elif mode == "block":
+        m = BLOCK_MODE
+        if kb.dim() != 4 or vb is None or vb.dim() != 4:
+            raise ValueError("block mode: k and v must be [pages, Hkv, page, D]")
+        num_kv, Hkv, page, _ = kb.shape
+        Dv = vb.shape[-1] if d_v is None else d_v
+        if idx.dim() != 3 or idx.shape[1] != T:
+            raise ValueError("block mode: indices must be [Hidx, T, topk]")
+        Hidx, topk = idx.shape[0], idx.shape[2]
+        bt = _i32t(block_table, "block_table")
+        cu = _i32t(cu_seqlens_q, "cu_seqlens_q")
+        sl = _i32t(seq_lens, "seq_lens")
+        B, max_blocks = bt.shape
+    else:
+        raise ValueError(f"mode must be 'token' or 'block', got {mode!r}")
+    tl = None if topk_length is None else _i32t(topk_length, "topk_length")
+    sink = None
+    if attn_sink is not None:
+        if attn_sink.dtype != torch.float32 or attn_sink.numel() != Hq:
+            raise ValueError("attn_sink must be float32 [Hq]")
+        sink = attn_sink.contiguous()
+    dev = qb.device
+    if out is None:
+        out = torch.empty((T, Hq, Dv), dtype=torch.bfloat16, device=dev)
+    if max_logits is None:
+        max_logits = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    need = lib.sparse_attn_workspace_size(m, B, T, int(max_q_len), Hq, Hkv, Hidx, Dv, topk, max_blocks)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd(m, _ptr(qb), _ptr(kb), _ptr(vb), num_kv, _ptr(idx), topk, _ptr(tl), _ptr(bt),
+                               max_blocks, _ptr(cu), _ptr(sl), B, T, int(max_q_len), Hq, Hkv, Hidx, Dqk, Dv,
+                               page, float(sm_scale), _scale(q_scale), _scale(k_scale), _scale(v_scale),
+                               _ptr(sink), _ptr(out), _ptr(max_logits), _ptr(lse), _ptr(workspace), wsz,
+                               _stream(stream)))
+    return out, max_logits, lse
+
+
+__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "load", "flatten_to_2d", "EXPORTED",
+           "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

@@ -1,0 +1,244 @@
+// C-ABI entry points: argument validation on the host, scale normalisation
+// (None -> unit, checked once at the launch boundary as the sglang PR 30971
+// digest prescribes in implementation step 3), then stream-ordered launches.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace fp8ts {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FP8TS_EHIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return FP8TS_OK;
+}
+
+// Optional scale: NULL -> (false, 1); otherwise must be finite and > 0.
+static int read_scale(const char *fn, const char *name, const float *s, bool *present, float *value) {
+  *present = s != nullptr;
+  *value = 1.0f;
+  if (!s) return FP8TS_OK;
+  const float v = *s;
+  if (!std::isfinite(v) || !(v > 0.0f)) return fail(FP8TS_EINVAL, "%s: %s must be finite and > 0 (got %g)", fn, name, (double)v);
+  *value = v;
+  return FP8TS_OK;
+}
+
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace fp8ts
+
+using namespace fp8ts;
+
+extern "C" {
+
+const char *fp8ts_last_error(void) { return g_last_error; }
+
+int fp8ts_abi_version(void) { return 1; }
+
+int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t x_row_stride,
+                 uint8_t *out, int64_t out_row_stride, const float *scale, hipStream_t stream) {
+  const char *fn = "fp8_quantize";
+  if (x_dtype != FP8TS_BF16 && x_dtype != FP8TS_FP16)
+    return fail(FP8TS_EINVAL, "%s: x_dtype must be 0 (bf16) or 1 (fp16), got %d", fn, x_dtype);
+  if (rows < 0 || cols < 0) return fail(FP8TS_EINVAL, "%s: negative shape (%lld, %lld)", fn, (long long)rows, (long long)cols);
+  bool has = false;
+  float sv = 1.0f;
+  if (int st = read_scale(fn, "scale", scale, &has, &sv)) return st;
+  if (rows == 0 || cols == 0) return FP8TS_OK;
+  if (!x || !out) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (x_row_stride < cols) return fail(FP8TS_EINVAL, "%s: x_row_stride %lld < cols %lld", fn, (long long)x_row_stride, (long long)cols);
+  if (out_row_stride < cols) return fail(FP8TS_EINVAL, "%s: out_row_stride %lld < cols %lld", fn, (long long)out_row_stride, (long long)cols);
+  const size_t xb = (size_t)((rows - 1) * x_row_stride + cols) * 2;
+  const size_t ob = (size_t)((rows - 1) * out_row_stride + cols);
+  if (overlaps(x, xb, out, ob)) return fail(FP8TS_EINVAL, "%s: out overlaps x", fn);
+  const float inv = has ? 1.0f / sv : 1.0f;   // fp32 reciprocal, rounded once
+  return launch_quantize(x, x_dtype, rows, cols, x_row_stride, out, out_row_stride, has, inv, stream);
+}
+
+size_t indexer_topk_workspace_size(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
+  if (total_q <= 0 || num_heads <= 0 || max_blocks <= 0) return 0;
+  return indexer_workspace_bytes(total_q, num_heads, max_blocks);
+}
+
+int indexer_topk(const uint8_t *idx_q, const uint8_t *idx_k, int64_t num_pages,
+                 const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
+                 const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
+                 int32_t num_heads, int32_t head_dim, int32_t page_size, float sm_scale,
+                 const float *idx_q_scale, const float *idx_k_scale, int32_t topk, int32_t *out_ids,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char *fn = "indexer_topk";
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || num_pages < 0 || max_blocks < 0)
+    return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  if (!(num_heads == 1 || num_heads == 2 || num_heads == 4 || num_heads == 8 || num_heads == 16))
+    return fail(FP8TS_EUNSUPPORTED, "%s: num_heads must be 1, 2, 4, 8 or 16 (got %d)", fn, num_heads);
+  if (head_dim != 128) return fail(FP8TS_EUNSUPPORTED, "%s: head_dim must be 128 (got %d)", fn, head_dim);
+  if (page_size != 128) return fail(FP8TS_EUNSUPPORTED, "%s: page_size must be 128 (got %d)", fn, page_size);
+  if (topk < 1 || topk > 64) return fail(FP8TS_EUNSUPPORTED, "%s: topk must be in [1, 64] (got %d)", fn, topk);
+  if (max_blocks > 4096) return fail(FP8TS_EUNSUPPORTED, "%s: max_blocks %d exceeds 4096", fn, max_blocks);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(FP8TS_EINVAL, "%s: sm_scale must be finite and > 0 (got %g)", fn, (double)sm_scale);
+  bool hq = false, hk = false;
+  float sq = 1.0f, sk = 1.0f;
+  if (int st = read_scale(fn, "idx_q_scale", idx_q_scale, &hq, &sq)) return st;
+  if (int st = read_scale(fn, "idx_k_scale", idx_k_scale, &hk, &sk)) return st;
+  if (total_q == 0) return FP8TS_OK;
+  if (batch == 0 || max_q_len == 0) return fail(FP8TS_EINVAL, "%s: total_q > 0 needs batch > 0 and max_q_len > 0", fn);
+  if (max_q_len > total_q) return fail(FP8TS_EINVAL, "%s: max_q_len %d > total_q %d", fn, max_q_len, total_q);
+  if (!idx_q || !idx_k || !block_table || !cu_seqlens_q || !seq_lens || !out_ids)
+    return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (max_blocks == 0 || num_pages == 0) return fail(FP8TS_EINVAL, "%s: empty KV cache / block table", fn);
+  const size_t need = indexer_workspace_bytes(total_q, num_heads, max_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(FP8TS_EINVAL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace ? workspace_bytes : 0);
+  if ((uintptr_t)workspace % 256) return fail(FP8TS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (overlaps(out_ids, (size_t)num_heads * total_q * topk * 4, idx_q, (size_t)total_q * num_heads * 128))
+    return fail(FP8TS_EINVAL, "%s: out_ids overlaps idx_q", fn);
+  IndexerArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_heads = num_heads;
+  a.topk = topk;
+  a.sigma = (float)((double)sm_scale * sq * sk);
+  a.out_ids = out_ids;
+  a.scores = static_cast<float *>(workspace);
+  return launch_indexer(a, stream);
+}
+
+size_t sparse_attn_workspace_size(int32_t mode, int32_t batch, int32_t total_q, int32_t max_q_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads,
+                                  int32_t head_dim_v, int32_t topk, int32_t max_blocks) {
+  if (total_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || topk <= 0) return 0;
+  if (mode == FP8TS_BLOCK_MODE && (num_idx_heads <= 0 || max_blocks <= 0 || max_q_len <= 0 || batch <= 0)) return 0;
+  return attn_workspace_bytes(mode, batch, total_q, max_q_len, num_q_heads, num_kv_heads, num_idx_heads,
+                              head_dim_v, topk, max_blocks);
+}
+
+int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v, int64_t num_kv,
+                    const int32_t *indices, int32_t topk, const int32_t *topk_length,
+                    const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
+                    const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads, int32_t head_dim_qk,
+                    int32_t head_dim_v, int32_t page_size, float sm_scale, const float *q_scale,
+                    const float *k_scale, const float *v_scale, const float *attn_sink, uint16_t *out,
+                    float *max_logits, float *lse, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const char *fn = "sparse_attn_fwd";
+  if (mode != FP8TS_TOKEN_MODE && mode != FP8TS_BLOCK_MODE)
+    return fail(FP8TS_EINVAL, "%s: mode must be 0 (token) or 1 (block), got %d", fn, mode);
+  if (total_q < 0 || num_kv < 0 || topk < 0 || batch < 0 || max_q_len < 0 || max_blocks < 0)
+    return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(FP8TS_EINVAL, "%s: num_q_heads %d must be a positive multiple of num_kv_heads %d", fn,
+                num_q_heads, num_kv_heads);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(FP8TS_EINVAL, "%s: sm_scale must be finite and > 0 (got %g)", fn, (double)sm_scale);
+  bool hq = false, hk = false, hv = false;
+  float sq = 1.0f, sk = 1.0f, sv = 1.0f;
+  if (int st = read_scale(fn, "q_scale", q_scale, &hq, &sq)) return st;
+  if (int st = read_scale(fn, "k_scale", k_scale, &hk, &sk)) return st;
+  if (int st = read_scale(fn, "v_scale", v_scale, &hv, &sv)) return st;
+
+  if (mode == FP8TS_TOKEN_MODE) {
+    if (head_dim_v != 512)
+      return fail(FP8TS_EUNSUPPORTED, "%s: token mode hard-codes d_v = 512 (got d_v=%d)", fn, head_dim_v);
+    if (head_dim_qk != 576)
+      return fail(FP8TS_EUNSUPPORTED, "%s: token mode needs head_dim_qk = 576 (got %d)", fn, head_dim_qk);
+    if (num_kv_heads != 1) return fail(FP8TS_EUNSUPPORTED, "%s: token mode has one shared KV head (got %d)", fn, num_kv_heads);
+    if (topk < 1) return fail(FP8TS_EINVAL, "%s: topk must be >= 1", fn);
+  } else {
+    if (head_dim_qk != 128 || head_dim_v != 128)
+      return fail(FP8TS_EUNSUPPORTED, "%s: block mode needs head_dim_qk = head_dim_v = 128 (got %d, %d)", fn,
+                  head_dim_qk, head_dim_v);
+    if (page_size != 128) return fail(FP8TS_EUNSUPPORTED, "%s: page_size must be 128 (got %d)", fn, page_size);
+    if (num_idx_heads <= 0 || num_q_heads % num_idx_heads)
+      return fail(FP8TS_EINVAL, "%s: num_q_heads %d must be a positive multiple of num_idx_heads %d", fn,
+                  num_q_heads, num_idx_heads);
+    const int G = num_q_heads / num_kv_heads, gqi = num_q_heads / num_idx_heads;
+    if (G % gqi && gqi % G)
+      return fail(FP8TS_EUNSUPPORTED, "%s: index-head groups (%d q heads) must nest with kv-head groups (%d)", fn,
+                  gqi, G);
+    if (G > 256) return fail(FP8TS_EUNSUPPORTED, "%s: more than 256 q heads per kv head", fn);
+    if (topk < 1 || topk > 64) return fail(FP8TS_EUNSUPPORTED, "%s: block mode topk must be in [1, 64] (got %d)", fn, topk);
+    if (max_blocks > 4096) return fail(FP8TS_EUNSUPPORTED, "%s: max_blocks %d exceeds 4096", fn, max_blocks);
+  }
+  if (total_q == 0) return FP8TS_OK;
+  if (!q || !k || !indices || !out || !max_logits || !lse) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (num_kv == 0) return fail(FP8TS_EINVAL, "%s: empty KV", fn);
+  if (mode == FP8TS_BLOCK_MODE) {
+    if (!v) return fail(FP8TS_EINVAL, "%s: block mode needs a V cache", fn);
+    if (!block_table || !cu_seqlens_q || !seq_lens || batch == 0 || max_blocks == 0 || max_q_len == 0)
+      return fail(FP8TS_EINVAL, "%s: block mode needs block_table, cu_seqlens_q, seq_lens, batch, max_blocks, max_q_len", fn);
+    if (max_q_len > total_q) return fail(FP8TS_EINVAL, "%s: max_q_len %d > total_q %d", fn, max_q_len, total_q);
+  }
+  const size_t need = attn_workspace_bytes(mode, batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                           num_idx_heads, head_dim_v, topk, max_blocks);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(FP8TS_EINVAL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace ? workspace_bytes : 0);
+  if (need && (uintptr_t)workspace % 256) return fail(FP8TS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  const size_t ob = (size_t)total_q * num_q_heads * head_dim_v * 2;
+  if (overlaps(out, ob, q, (size_t)total_q * num_q_heads * head_dim_qk))
+    return fail(FP8TS_EINVAL, "%s: out overlaps q", fn);
+
+  AttnArgs a{};
+  a.mode = mode;
+  a.q = q;
+  a.k = k;
+  a.v = v ? v : k;
+  a.num_kv = num_kv;
+  a.k_row_stride = head_dim_qk;
+  a.v_row_stride = v ? head_dim_v : head_dim_qk;
+  a.indices = indices;
+  a.topk = topk;
+  a.topk_length = topk_length;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.hidx = mode == FP8TS_BLOCK_MODE ? num_idx_heads : 1;
+  a.dqk = head_dim_qk;
+  a.dv = head_dim_v;
+  // q_scale folds into sm_scale; it reaches both the key logits and the sink,
+  // k_scale only the key logits.  Products taken in double, rounded once.
+  const double s = (double)sm_scale * (double)sq;
+  a.key_scale_log2 = (float)(s * (double)sk * 1.4426950408889634);
+  a.sink_scale_log2 = (float)(s * 1.4426950408889634);
+  a.v_scale = sv;
+  a.sink = attn_sink;
+  a.out = out;
+  a.max_logits = max_logits;
+  a.lse = lse;
+  a.workspace = workspace;
+  return launch_attention(a, stream);
+}
+
+}  // extern "C"

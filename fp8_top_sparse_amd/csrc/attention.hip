@@ -1,0 +1,638 @@
+// Sparse attention forward over selected KV tokens (token mode) or blocks
+// (block mode), e4m3 Q/K/V, bf16 output, fp32 max_logits / lse.
+//
+// Semantics: sglang PR 25751 digest (code excerpt of
+// sparse_mla_q8kv8_prefill_fwd: out [s_q, h_q, d_v] bf16, max_logits and lse
+// [s_q, h_q] fp32, optional attn_sink and topk_length, d_v = 512 for MLA) and
+// sglang PR 30971 digest (summary and implementation step 3: q_scale folded
+// into sm_scale so it scales the QK dot and the sink logit, k_scale never
+// touches the sink, v_scale on the output, None = unit).
+//
+// Design (gfx950, wave64):
+//  * A workgroup owns ROWS = WAVES * COLS * 16 query rows.  Block mode: rows
+//    are (token, head) pairs of one KV head (all heads sharing that KV head,
+//    for a tile of consecutive tokens), so one staged K/V block serves every
+//    row; token mode: rows are the heads of one query token, which share its
+//    index list.
+//  * Keys are staged in LDS per tile (block mode: one 128-token page of one KV
+//    head, 16 KB contiguous; token mode: 64 gathered KV rows).  V is widened
+//    to bf16 and transposed on the way into LDS so that the PV operand is
+//    key-contiguous.
+//  * S^T = K Q^T on 16x16x128 e4m3 MFMA (plus 16x16x32 e4m3 for the 64-wide
+//    tail of d_qk = 576): each lane then holds 4 keys of one query row, which
+//    is exactly the B-operand layout of the PV product, so P never leaves
+//    registers.  PV runs on 16x16x32 bf16 MFMA with P in bf16: rounding P to
+//    e4m3 (the pages' design) costs ~3% of max|out|, above the 2e-2 budget.
+//  * Online softmax in the log2 domain with lazy rescaling: the reference
+//    maximum only moves when a new tile maximum exceeds it by 2^8, so most
+//    tiles skip the accumulator rescale.  The row sum L is accumulated from
+//    the fp32 probabilities.
+//  * Block mode: every row's block list becomes an LDS bitmap; the workgroup
+//    walks the union of its rows' lists in ascending order and masks rows
+//    that did not select the current block.  Keys j > p are masked (causal).
+//  * Decode and small token-mode workloads split the key list across
+//    workgroups; partial (O, m, l) go to the workspace and a combine kernel
+//    merges them by log-sum-exp.
+#include "device.h"
+#include "internal.h"
+
+namespace fp8ts {
+namespace {
+
+constexpr int kPage = 128;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+
+struct Grid {
+  int n_tiles;   // query tiles per sequence (block) / head groups (token)
+  int splits;    // key-list splits (1 = write final outputs directly)
+  int G;         // block: q heads per kv head
+  int TT;        // block: tokens per tile
+  int gqi;       // block: q heads per index head
+  int n_il;      // block: index heads per kv head tile
+  int NL;        // block: lists per workgroup
+  int W;         // block: 32-bit words per block bitmap
+  float *part_o;   // [splits, T, Hq, DV]
+  float *part_ml;  // [splits, T, Hq, 4] = (m_used, l, m_true, -)
+};
+
+__device__ __forceinline__ v8i lds_read32(const uint8_t *p) {
+  const v4i *q = reinterpret_cast<const v4i *>(p);
+  v4i lo = q[0], hi = q[1];
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ v8i gload32(const uint8_t *p) {
+  const v4i *q = reinterpret_cast<const v4i *>(p);
+  v4i lo = q[0], hi = q[1];
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Stage one 4-key x 16-dim unit of V (e4m3, rows `rows[0..3]`) into V^T (bf16).
+__device__ __forceinline__ void stage_v_unit(uint8_t *vt, int vpitch, int key0, int d0,
+                                             const uint8_t *r0, const uint8_t *r1,
+                                             const uint8_t *r2, const uint8_t *r3) {
+  const v4i w0 = *reinterpret_cast<const v4i *>(r0);
+  const v4i w1 = *reinterpret_cast<const v4i *>(r1);
+  const v4i w2 = *reinterpret_cast<const v4i *>(r2);
+  const v4i w3 = *reinterpret_cast<const v4i *>(r3);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {       // dword q covers dims d0 + 4q .. 4q + 3
+    v4bf c0 = e4m3x4_to_bf16(w0[q]);
+    v4bf c1 = e4m3x4_to_bf16(w1[q]);
+    v4bf c2 = e4m3x4_to_bf16(w2[q]);
+    v4bf c3 = e4m3x4_to_bf16(w3[q]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v4bf col = {c0[j], c1[j], c2[j], c3[j]};
+      *reinterpret_cast<v4bf *>(vt + (d0 + 4 * q + j) * vpitch + 2 * key0) = col;
+    }
+  }
+}
+
+// Dynamic LDS layout sizes.
+template <int DQK, int DV, int KT>
+struct Lds {
+  static constexpr int KP = DQK + 16;          // K row pitch (bytes)
+  static constexpr int VP = 2 * KT + 16;       // V^T row pitch (bytes)
+  static constexpr int K_BYTES = KT * KP;
+  static constexpr int V_BYTES = DV * VP;
+  static constexpr int IDX_OFF = K_BYTES + V_BYTES;
+  static constexpr int BASE = IDX_OFF + KT * 4;
+};
+
+template <int DQK, int DV, int WAVES, int COLS, int KT, bool BLOCK>
+__global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
+  static_assert(DQK % 128 == 0 || DQK % 128 == 64, "d_qk must be a multiple of 64");
+  static_assert(DV % 16 == 0 && KT % 64 == 0, "tile shape");
+  constexpr int NT = WAVES * 64;
+  constexpr int NKC = DQK / 128;               // full 128-wide K slices
+  constexpr bool TAIL = (DQK % 128) == 64;
+  constexpr int NDT = DV / 16;
+  using L = Lds<DQK, DV, KT>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t *kt_s = smem;
+  uint8_t *vt_s = smem + L::K_BYTES;
+  int32_t *idx_s = reinterpret_cast<int32_t *>(smem + L::IDX_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int64_t T = a.total_q;
+
+  // ---------------------------------------------------------------- work item
+  int bid = blockIdx.x;
+  const int split = bid % gr.splits;
+  bid /= gr.splits;
+
+  // per-row metadata for the lane's column in each of its column tiles
+  int row_t[COLS], row_h[COLS], row_p[COLS], row_li[COLS];
+  bool row_ok[COLS];
+
+  // block mode
+  int b = 0, kvh = 0, cu0 = 0, q_len = 0, seq_len = 0, t0 = 0;
+  uint32_t *bits = nullptr;      // [NL][W] list bitmaps, then [W] union
+  int32_t *ulist = nullptr;      // ascending union of block ids
+  int32_t *ucount = nullptr;
+  // token mode
+  int tok = 0, list_len = 0;
+
+  int range_lo = 0, range_hi = 0;  // positions (union list / index list) of this split
+
+  if constexpr (BLOCK) {
+    kvh = bid % a.hkv;
+    bid /= a.hkv;
+    b = bid % a.batch;
+    const int tile = gr.n_tiles - 1 - bid / a.batch;
+    // sequence range, clamped to [0, total_q) whatever the device metadata holds
+    cu0 = min(max(a.cu_seqlens_q[b], 0), a.total_q);
+    q_len = min(max(a.cu_seqlens_q[b + 1] - cu0, 0), a.total_q - cu0);
+    seq_len = a.seq_lens[b];
+    t0 = tile * gr.TT;
+    if (t0 >= q_len) return;
+    const int gi_lo = (kvh * gr.G) / gr.gqi;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) {
+      const int r = (wave * COLS + c) * 16 + col;
+      const int tt = t0 + r / gr.G;
+      const int h = kvh * gr.G + r % gr.G;
+      // rows past TT * G (when G does not divide the tile) belong to no token
+      row_ok[c] = (r / gr.G) < gr.TT && tt < q_len;
+      row_t[c] = cu0 + tt;
+      row_h[c] = h;
+      row_p[c] = row_ok[c] ? seq_len - q_len + tt : -1;
+      row_li[c] = row_ok[c] ? (r / gr.G) * gr.n_il + (h / gr.gqi - gi_lo) : 0;
+    }
+    bits = reinterpret_cast<uint32_t *>(smem + L::BASE);
+    uint32_t *ubits = bits + gr.NL * gr.W;
+    ucount = reinterpret_cast<int32_t *>(ubits + gr.W);
+    ulist = ucount + 4;
+    for (int w = tid; w < (gr.NL + 1) * gr.W; w += NT) bits[w] = 0u;
+    __syncthreads();
+    const int nsel = gr.NL * a.topk;
+    for (int e = tid; e < nsel; e += NT) {
+      const int li = e / a.topk;
+      const int j = e - li * a.topk;
+      const int tt = t0 + li / gr.n_il;
+      const int gi = gi_lo + li % gr.n_il;
+      if (tt >= q_len) continue;
+      const int p = seq_len - q_len + tt;
+      const int id = a.indices[((int64_t)gi * T + cu0 + tt) * a.topk + j];
+      if (id < 0 || id >= a.max_blocks || (int64_t)id * kPage > p) continue;
+      atomicOr(&bits[li * gr.W + (id >> 5)], 1u << (id & 31));
+      atomicOr(&ubits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    // wave 0: exclusive scan of the union words' popcounts, then emit ids ascending
+    if (wave == 0) {
+      int running = 0;
+      for (int w0 = 0; w0 < gr.W; w0 += 64) {
+        const int w = w0 + lane;
+        const uint32_t word = w < gr.W ? ubits[w] : 0u;
+        int cnt = __popc(word);
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          int v = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += v;
+        }
+        int pos = running + incl - cnt;
+        uint32_t m = word;
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          ulist[pos++] = w * 32 + bit;
+          m &= m - 1;
+        }
+        running += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) ucount[0] = running;
+    }
+    __syncthreads();
+    const int U = ucount[0];
+    const int chunk = (U + gr.splits - 1) / gr.splits;
+    range_lo = min(U, split * chunk);
+    range_hi = min(U, range_lo + chunk);
+  } else {
+    const int hg = bid % gr.n_tiles;
+    tok = bid / gr.n_tiles;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) {
+      const int r = (wave * COLS + c) * 16 + col;
+      const int h = hg * (WAVES * COLS * 16) + r;
+      row_ok[c] = h < a.hq;
+      row_t[c] = tok;
+      row_h[c] = h;
+      row_p[c] = 0;
+      row_li[c] = 0;
+    }
+    list_len = a.topk;
+    if (a.topk_length) list_len = max(0, min(a.topk, a.topk_length[tok]));
+    const int chunk = ((list_len + gr.splits - 1) / gr.splits + KT - 1) / KT * KT;
+    range_lo = min(list_len, split * chunk);
+    range_hi = min(list_len, range_lo + chunk);
+  }
+
+  // ---------------------------------------------------------------- Q operands
+  v8i qb[COLS][NKC > 0 ? NKC : 1];
+  long qt[COLS][2];
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    const int64_t qr = row_ok[c] ? (int64_t)row_t[c] * a.hq + row_h[c] : 0;
+    const uint8_t *qrow = a.q + qr * DQK;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      qb[c][kc] = row_ok[c] ? gload32(qrow + 128 * kc + 32 * g) : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        qt[c][mm] = row_ok[c] ? *reinterpret_cast<const long *>(qrow + NKC * 128 + 32 * mm + 8 * g) : 0;
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- state
+  v4f o[NDT][COLS];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_used[COLS], m_true[COLS], lsum[COLS];
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    m_used[c] = -INFINITY;
+    m_true[c] = -INFINITY;
+    lsum[c] = 0.f;
+  }
+  const float ck = a.key_scale_log2;
+
+  // ---------------------------------------------------------------- key tiles
+  const int n_iter = BLOCK ? (range_hi - range_lo) : (range_hi - range_lo + KT - 1) / KT;
+  for (int it = 0; it < n_iter; ++it) {
+    int blk = 0;
+    int key_base = 0;        // absolute key position of tile row 0 (block mode)
+    int n_valid_keys = KT;
+    __syncthreads();         // previous tile fully consumed
+    if constexpr (BLOCK) {
+      blk = ulist[range_lo + it];
+      const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
+      if (page < 0 || page >= a.num_kv) continue;   // uniform: no keys from this block
+      key_base = blk * kPage;
+      const uint8_t *kp = a.k + ((int64_t)page * a.hkv + kvh) * kPage * DQK;
+      const uint8_t *vp = a.v + ((int64_t)page * a.hkv + kvh) * kPage * DV;
+      for (int ch = tid; ch < KT * (DQK / 16); ch += NT) {
+        const int key = ch / (DQK / 16);
+        const int part = ch - key * (DQK / 16);
+        *reinterpret_cast<v4i *>(kt_s + key * L::KP + 16 * part) =
+            *reinterpret_cast<const v4i *>(kp + key * DQK + 16 * part);
+      }
+      for (int u = tid; u < (KT / 4) * (DV / 16); u += NT) {
+        const int kg = u / (DV / 16);
+        const int dg = u - kg * (DV / 16);
+        const uint8_t *r = vp + (4 * kg) * DV + 16 * dg;
+        stage_v_unit(vt_s, L::VP, 4 * kg, 16 * dg, r, r + DV, r + 2 * DV, r + 3 * DV);
+      }
+    } else {
+      const int pos0 = range_lo + it * KT;
+      for (int j = tid; j < KT; j += NT) {
+        int id = -1;
+        if (pos0 + j < range_hi) {
+          id = a.indices[(int64_t)tok * a.topk + pos0 + j];
+          if (id < 0 || id >= a.num_kv) id = -1;
+        }
+        idx_s[j] = id;
+      }
+      __syncthreads();
+      n_valid_keys = 0;
+      for (int j = 0; j < KT; ++j) n_valid_keys += idx_s[j] >= 0;
+      for (int ch = tid; ch < KT * (DQK / 16); ch += NT) {
+        const int key = ch / (DQK / 16);
+        const int part = ch - key * (DQK / 16);
+        const int id = idx_s[key];
+        v4i val = {0, 0, 0, 0};
+        if (id >= 0) val = *reinterpret_cast<const v4i *>(a.k + (int64_t)id * a.k_row_stride + 16 * part);
+        *reinterpret_cast<v4i *>(kt_s + key * L::KP + 16 * part) = val;
+      }
+      for (int u = tid; u < (KT / 4) * (DV / 16); u += NT) {
+        const int kg = u / (DV / 16);
+        const int dg = u - kg * (DV / 16);
+        const uint8_t *rr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int id = idx_s[4 * kg + q];
+          // absent keys read row 0 (any finite bytes); their P is exactly 0
+          rr[q] = a.v + (int64_t)(id >= 0 ? id : 0) * a.v_row_stride + 16 * dg;
+        }
+        stage_v_unit(vt_s, L::VP, 4 * kg, 16 * dg, rr[0], rr[1], rr[2], rr[3]);
+      }
+    }
+    __syncthreads();
+
+    // per-row mask bound for this tile: key position must be <= lim
+    int lim[COLS];
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) {
+      if constexpr (BLOCK) {
+        const bool sel = row_ok[c] && ((bits[row_li[c] * gr.W + (blk >> 5)] >> (blk & 31)) & 1u);
+        lim[c] = sel ? row_p[c] : -1;
+      } else {
+        lim[c] = row_ok[c] ? 0x7fffffff : -1;
+      }
+    }
+
+#pragma unroll 1
+    for (int koff = 0; koff < KT; koff += 64) {
+      // ---- S^T = K Q^T for 64 keys
+      v4f s[4][COLS];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) s[kt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+        const uint8_t *krow = kt_s + (koff + kt * 16 + col) * L::KP;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const v8i ka = lds_read32(krow + 128 * kc + 32 * g);
+#pragma unroll
+          for (int c = 0; c < COLS; ++c) s[kt][c] = mfma_16x16x128_e4m3(ka, qb[c][kc], s[kt][c]);
+        }
+        if constexpr (TAIL) {
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const long ka = *reinterpret_cast<const long *>(krow + NKC * 128 + 32 * mm + 8 * g);
+#pragma unroll
+            for (int c = 0; c < COLS; ++c) s[kt][c] = mfma_16x16x32_e4m3(ka, qt[c][mm], s[kt][c]);
+          }
+        }
+      }
+      // ---- masks
+      const bool tile_has_invalid = !BLOCK && n_valid_keys < KT;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kl = koff + kt * 16 + 4 * g + i;
+          if constexpr (BLOCK) {
+            const int pos = key_base + kl;
+#pragma unroll
+            for (int c = 0; c < COLS; ++c)
+              if (pos > lim[c]) s[kt][c][i] = -INFINITY;
+          } else {
+            const bool kv_ok = !tile_has_invalid || idx_s[kl] >= 0;
+#pragma unroll
+            for (int c = 0; c < COLS; ++c)
+              if (!kv_ok || lim[c] < 0) s[kt][c][i] = -INFINITY;
+          }
+        }
+      }
+      // ---- online softmax (log2 domain, lazy rescale)
+      v8bf pb[COLS][2];
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) {
+        float smax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) smax = fmaxf(smax, s[kt][c][i]);
+        smax = group4_max(smax);
+        const float mt = smax * ck;
+        m_true[c] = fmaxf(m_true[c], mt);
+        if (mt > m_used[c] + kTau) {
+          const float alpha = exp2f(m_used[c] - mt);
+          lsum[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[dt][c] *= alpha;
+          m_used[c] = mt;
+        }
+        const float msub = m_used[c] == -INFINITY ? 0.f : m_used[c];
+        float p[4][4];
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[kt][i] = exp2f(fmaf(s[kt][c][i], ck, -msub));
+            ls += p[kt][i];
+          }
+        lsum[c] += ls;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          v8bf v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = (__bf16)p[2 * m][i];
+            v[4 + i] = (__bf16)p[2 * m + 1][i];
+          }
+          pb[c][m] = v;
+        }
+      }
+      // ---- O^T += V^T P^T (bf16 MFMA, 32 keys per step)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint8_t *vrow = vt_s + (dt * 16 + col) * L::VP + 2 * (koff + 32 * m + 4 * g);
+          const v4bf lo = *reinterpret_cast<const v4bf *>(vrow);
+          const v4bf hi = *reinterpret_cast<const v4bf *>(vrow + 32);
+          const v8bf va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int c = 0; c < COLS; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[c][m], o[dt][c]);
+        }
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    const float l_tot = group4_sum(lsum[c]);
+    if (!row_ok[c]) continue;
+    const int64_t rowidx = (int64_t)row_t[c] * a.hq + row_h[c];
+    if (gr.splits > 1) {
+      float *po = gr.part_o + ((int64_t)split * T * a.hq + rowidx) * DV;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<v4f *>(po + dt * 16 + 4 * g) = o[dt][c];
+      if (g == 0) {
+        float *pm = gr.part_ml + ((int64_t)split * T * a.hq + rowidx) * 4;
+        *reinterpret_cast<v4f *>(pm) = (v4f){m_used[c], l_tot, m_true[c], 0.f};
+      }
+      continue;
+    }
+    const bool has_sink = a.sink != nullptr;
+    const float zs = has_sink ? a.sink_scale_log2 * a.sink[row_h[c]] : -INFINITY;
+    const float M = fmaxf(m_used[c], zs);
+    float Lt = 0.f, fo = 0.f;
+    if (M != -INFINITY) {
+      const float wk = m_used[c] == -INFINITY ? 0.f : exp2f(m_used[c] - M);
+      Lt = l_tot * wk + (has_sink ? exp2f(zs - M) : 0.f);
+      fo = Lt > 0.f ? wk * a.v_scale / Lt : 0.f;
+    }
+    uint16_t *orow = a.out + rowidx * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const v4f x = o[dt][c] * fo;
+      uint2 pk = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+      *reinterpret_cast<uint2 *>(orow + dt * 16 + 4 * g) = pk;
+    }
+    if (g == 0) {
+      a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+      a.max_logits[rowidx] = m_true[c] * kLn2;
+    }
+  }
+}
+
+// Merge split partials: out = v_scale * sum_s O_s 2^(m_s - M) / L.
+template <int DV>
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) {
+  const int64_t rowidx = blockIdx.x;            // t * hq + h
+  const int h = (int)(rowidx % a.hq);
+  const int64_t TH = (int64_t)a.total_q * a.hq;
+  const bool has_sink = a.sink != nullptr;
+  const float zs = has_sink ? a.sink_scale_log2 * a.sink[h] : -INFINITY;
+  float M = zs, mtrue = -INFINITY;
+  for (int s = 0; s < gr.splits; ++s) {
+    const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
+    M = fmaxf(M, pm[0]);
+    mtrue = fmaxf(mtrue, pm[2]);
+  }
+  float Lt = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < gr.splits; ++s) {
+      const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
+      if (pm[0] != -INFINITY) Lt += pm[1] * exp2f(pm[0] - M);
+    }
+    if (has_sink) Lt += exp2f(zs - M);
+  }
+  const float scale = Lt > 0.f ? a.v_scale / Lt : 0.f;
+  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
+    float acc = 0.f;
+    if (Lt > 0.f) {
+      for (int s = 0; s < gr.splits; ++s) {
+        const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
+        if (pm[0] != -INFINITY) acc += gr.part_o[(s * TH + rowidx) * DV + d] * exp2f(pm[0] - M);
+      }
+    }
+    a.out[rowidx * DV + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * scale));
+  }
+  if (threadIdx.x == 0) {
+    a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+    a.max_logits[rowidx] = mtrue * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+struct Plan {
+  int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads
+  Grid gr;
+  int64_t nblocks;
+  size_t lds;
+  size_t ws;
+};
+
+template <int DQK, int DV, int KT>
+constexpr size_t lds_base() { return Lds<DQK, DV, KT>::BASE; }
+
+Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv, int hidx,
+               int dv, int topk, int max_blocks) {
+  Plan pl{};
+  Grid &gr = pl.gr;
+  gr.splits = 1;
+  if (mode == FP8TS_BLOCK_MODE) {
+    gr.G = hq / hkv;
+    gr.gqi = hq / hidx;
+    gr.W = (max_blocks + 31) / 32;
+    const bool decode = (int64_t)max_q_len * gr.G <= 16;
+    const int rows = decode ? 16 : 256;
+    gr.TT = rows / gr.G;
+    if (gr.TT < 1) gr.TT = 1;
+    gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
+    // index heads touched by the q heads of one kv head
+    const int gi_lo = 0, gi_hi = (gr.G - 1) / gr.gqi;
+    gr.n_il = gr.G >= gr.gqi ? gr.G / gr.gqi : 1;
+    (void)gi_lo;
+    (void)gi_hi;
+    gr.NL = gr.TT * gr.n_il;
+    if (decode) {
+      pl.kind = 1;
+      // split the union (at most n_il * topk blocks) into chunks of ~8 blocks
+      int ubound = gr.n_il * topk;
+      if (ubound > max_blocks) ubound = max_blocks;
+      gr.splits = (ubound + 7) / 8;
+      if (gr.splits < 1) gr.splits = 1;
+    } else {
+      pl.kind = 0;
+    }
+    pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+    pl.lds = lds_base<128, 128, 128>() +
+             4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
+  } else {
+    if (hq % 128 == 0) {
+      pl.kind = 2;
+      gr.n_tiles = hq / 128;
+      gr.splits = 1;
+      pl.lds = lds_base<576, 512, 64>();
+    } else {
+      pl.kind = 3;
+      gr.n_tiles = (hq + 15) / 16;
+      // split the list so that tiny workloads still fill the GPU
+      const int per = (topk + 63) / 64;
+      gr.splits = per > 8 ? 8 : per;
+      if ((int64_t)total_q * gr.n_tiles >= 2048) gr.splits = 1;
+      pl.lds = lds_base<576, 512, 64>();
+    }
+    pl.nblocks = (int64_t)gr.splits * total_q * gr.n_tiles;
+  }
+  if (gr.splits > 1) {
+    pl.ws = (size_t)gr.splits * total_q * hq * dv * 4 + (size_t)gr.splits * total_q * hq * 16 + 256;
+  }
+  return pl;
+}
+
+template <typename K>
+int launch_k(K kern, const Plan &pl, int threads, const AttnArgs &a, hipStream_t stream) {
+  if (pl.lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+    if (e != hipSuccess) return fail(FP8TS_EHIP, "sparse_attn_fwd: LDS attribute: %s", hipGetErrorString(e));
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)pl.nblocks), dim3(threads), pl.lds, stream, a, pl.gr);
+  return check_launch("sparse_attn_fwd");
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int32_t mode, int32_t batch, int32_t total_q, int32_t max_q_len,
+                            int32_t hq, int32_t hkv, int32_t hidx, int32_t dv, int32_t topk,
+                            int32_t max_blocks) {
+  return make_plan(mode, batch, total_q, max_q_len, hq, hkv, hidx, dv, topk, max_blocks).ws;
+}
+
+int launch_attention(const AttnArgs &a, hipStream_t stream) {
+  if (a.total_q == 0) return FP8TS_OK;
+  Plan pl = make_plan(a.mode, a.batch, a.total_q, a.max_q_len, a.hq, a.hkv, a.hidx, a.dv, a.topk,
+                      a.max_blocks);
+  if (pl.gr.splits > 1) {
+    uint8_t *ws = static_cast<uint8_t *>(a.workspace);
+    pl.gr.part_o = reinterpret_cast<float *>(ws);
+    pl.gr.part_ml = reinterpret_cast<float *>(ws + (size_t)pl.gr.splits * a.total_q * a.hq * a.dv * 4);
+  }
+  if (pl.nblocks == 0) return FP8TS_OK;
+  int st = FP8TS_OK;
+  switch (pl.kind) {
+    case 0: st = launch_k(attn_kernel<128, 128, 4, 4, 128, true>, pl, 256, a, stream); break;
+    case 1: st = launch_k(attn_kernel<128, 128, 1, 1, 128, true>, pl, 64, a, stream); break;
+    case 2: st = launch_k(attn_kernel<576, 512, 8, 1, 64, false>, pl, 512, a, stream); break;
+    default: st = launch_k(attn_kernel<576, 512, 1, 1, 64, false>, pl, 64, a, stream); break;
+  }
+  if (st || pl.gr.splits == 1) return st;
+  if (a.dv == 512) {
+    hipLaunchKernelGGL(attn_combine_kernel<512>, dim3((unsigned)((int64_t)a.total_q * a.hq)), dim3(128), 0,
+                       stream, a, pl.gr);
+  } else {
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)((int64_t)a.total_q * a.hq)), dim3(128), 0,
+                       stream, a, pl.gr);
+  }
+  return check_launch("sparse_attn_fwd (combine)");
+}
+
+}  // namespace fp8ts

@@ -1,0 +1,95 @@
+// Device-side building blocks for gfx950 (CDNA4): MFMA wrappers, fp8/bf16
+// conversions and wave64 helpers.  Everything here is written for 64-lane
+// wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8ts {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- MFMA
+// Operand layout used throughout (16x16 output tiles, wave64):
+//   A (16 x K): lane l holds row (l % 16), K-slice (l / 16)
+//   B (K x 16): lane l holds column (l % 16), the same K-slice (l / 16)
+//   D (16 x 16): lane l, register i holds row 4 * (l / 16) + i, column l % 16
+// The contraction index is permuted identically in A and B, so any consistent
+// assignment of K elements to (lane group, byte) is a valid operand layout.
+
+// D += A(16x128, e4m3) * B(128x16, e4m3); lane K-slice = 32 bytes.
+// cbsz = blgp = 0 selects OCP e4m3 for both operands; E8M0 scales 127 = 1.0.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i &a, const v8i &b, const v4f &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// D += A(16x32, e4m3) * B(32x16, e4m3); lane K-slice = 8 bytes.
+__device__ __forceinline__ v4f mfma_16x16x32_e4m3(long a, long b, const v4f &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+// D += A(16x32, bf16) * B(32x16, bf16); lane K-slice = 8 bf16.
+__device__ __forceinline__ v4f mfma_16x16x32_bf16(const v8bf &a, const v8bf &b, const v4f &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+// Two e4m3 bytes of `packed` (selected half: hi = bytes 2,3) -> two floats, exact.
+__device__ __forceinline__ v2f e4m3x2_to_f32(int packed, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(packed, true)
+            : __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
+}
+
+// Four e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ v4bf e4m3x4_to_bf16(int packed) {
+  v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
+  v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(packed, true);
+  v4bf r;
+  r[0] = (__bf16)lo[0];
+  r[1] = (__bf16)lo[1];
+  r[2] = (__bf16)hi[0];
+  r[3] = (__bf16)hi[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  v2bf r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------- wave64
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Butterfly over lanes l ^ mask (mask < 64) via ds_bpermute (no LDS storage used).
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+  int src = (lane_id() ^ mask) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+}
+
+// Max / sum over the four lane groups (l, l^16, l^32, l^48) that hold the same
+// MFMA column.
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, shfl_xor_f32(v, 16));
+  v = fmaxf(v, shfl_xor_f32(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += shfl_xor_f32(v, 16);
+  v += shfl_xor_f32(v, 32);
+  return v;
+}
+
+}  // namespace fp8ts

@@ -1,0 +1,67 @@
+// Host-side internals shared by the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fp8ts.h"
+
+namespace fp8ts {
+
+// Records a formatted message as the thread's last error and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Returns FP8TS_OK, or FP8TS_EHIP with a message if the last launch failed.
+int check_launch(const char *what);
+
+// ---- quantize
+int launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_stride,
+                    uint8_t *out, int64_t out_stride, bool has_scale, float scale_inv,
+                    hipStream_t stream);
+
+// ---- indexer
+struct IndexerArgs {
+  const uint8_t *idx_q;
+  const uint8_t *idx_k;
+  int64_t num_pages;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  const int32_t *cu_seqlens_q;
+  const int32_t *seq_lens;
+  int32_t batch, total_q, max_q_len, num_heads, topk;
+  float sigma;  // sm_scale * idx_q_scale * idx_k_scale (> 0)
+  int32_t *out_ids;
+  float *scores;  // workspace [num_heads, total_q, max_blocks]
+};
+size_t indexer_workspace_bytes(int32_t total_q, int32_t num_heads, int32_t max_blocks);
+int launch_indexer(const IndexerArgs &a, hipStream_t stream);
+
+// ---- attention
+struct AttnArgs {
+  int32_t mode;
+  const uint8_t *q, *k, *v;
+  int64_t num_kv;
+  int64_t k_row_stride, v_row_stride;  // token mode: bytes between KV rows
+  const int32_t *indices;
+  int32_t topk;
+  const int32_t *topk_length;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  const int32_t *cu_seqlens_q, *seq_lens;
+  int32_t batch, total_q, max_q_len;
+  int32_t hq, hkv, hidx, dqk, dv;
+  float key_scale_log2;   // sm * q_scale * k_scale * log2(e)
+  float sink_scale_log2;  // sm * q_scale * log2(e)
+  float v_scale;
+  const float *sink;
+  uint16_t *out;
+  float *max_logits, *lse;
+  void *workspace;
+};
+size_t attn_workspace_bytes(int32_t mode, int32_t batch, int32_t total_q, int32_t max_q_len,
+                            int32_t hq, int32_t hkv, int32_t hidx, int32_t dv, int32_t topk,
+                            int32_t max_blocks);
+int launch_attention(const AttnArgs &a, hipStream_t stream);
+
+}  // namespace fp8ts

@@ -1,0 +1,207 @@
+/*
+ * fp8ts.h - C ABI of the FP8-e4m3 top-k sparse attention library (libfp8ts.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, in the order a sparse-attention layer calls them:
+ *
+ *   fp8_quantize     per-tensor e4m3 quantization of the queries and the index
+ *                    query (stored value = x / scale, None = unit scale).
+ *   indexer_topk     lightning indexer: scores every 128-token KV block by the
+ *                    maximum index logit over its visible tokens and writes the
+ *                    top-k block ids of every (index head, query) in strictly
+ *                    ascending order, -1 padded.
+ *   sparse_attn_fwd  attention over only the selected KV tokens (token mode,
+ *                    MLA-style) or blocks (block mode, paged GQA), with online
+ *                    softmax, optional attention sink, bf16 output and fp32
+ *                    max_logits / lse.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers must point to device memory of the
+ *   current HIP device; "host" pointers are read during the call only.
+ * - Every fp8 tensor is OCP e4m3fn, passed as raw bytes (uint8_t).  No other
+ *   fp8 format is accepted: the pages forbid e5m2 on this path (sglang PR 30971
+ *   digest, implementation step 1: e5m2 must never reach the fp8 attention
+ *   kernel).
+ * - Optional per-tensor scales are host pointers to one float: NULL means
+ *   "None", i.e. unit scale with the multiply skipped (sglang PR 30971 digest,
+ *   implementation steps 3 and 4).  A given scale must be finite and > 0.
+ * - Ownership: the caller owns every input, output and workspace buffer.  The
+ *   library allocates nothing per call, keeps no output cache and never
+ *   writes its inputs (sglang PR 25751 digest, review thread on output
+ *   aliasing).  Outputs are written in full, so they may be uninitialised
+ *   ("empty", sglang PR 25460 digest, implementation step 4).  Outputs must
+ *   not alias inputs.
+ * - Streams: all work is enqueued asynchronously on `stream` (0 = the null
+ *   stream).  No call synchronises, copies between host and device or
+ *   allocates, so calls may be captured into a HIP graph.
+ * - Errors: arguments are validated on the host before anything is launched.
+ *   On failure the call returns a non-zero status, launches nothing, and
+ *   fp8ts_last_error() describes the failure (thread-local string, valid until
+ *   the next failing call on the same thread).  HIP launch failures return
+ *   FP8TS_EHIP.  Device-side values (index lists, block tables, sequence
+ *   lengths) cannot be validated without a copy: out-of-range entries are
+ *   ignored by the kernels (treated as absent) rather than dereferenced.
+ */
+#ifndef FP8TS_H
+#define FP8TS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp8ts_status {
+  FP8TS_OK = 0,
+  FP8TS_EINVAL = 1,      /* malformed argument (null pointer, bad size, bad scale, ...) */
+  FP8TS_EUNSUPPORTED = 2,/* well-formed but outside what the kernels implement */
+  FP8TS_EHIP = 3         /* the HIP runtime reported an error */
+};
+
+enum fp8ts_dtype { FP8TS_BF16 = 0, FP8TS_FP16 = 1 };
+
+enum fp8ts_attn_mode {
+  FP8TS_TOKEN_MODE = 0, /* per-query token indices into a flat KV array (MLA) */
+  FP8TS_BLOCK_MODE = 1  /* per-(index head, query) block ids into paged K/V (GQA) */
+};
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *fp8ts_last_error(void);
+
+/* ABI version of this header (incremented on any signature change). */
+int fp8ts_abi_version(void);
+
+/*
+ * fp8_quantize - y = e4m3(fl32(fl32(x) * fl32(1 / scale))), per tensor.
+ *
+ * Follows the quantize kernel of the sglang PR 25460 digest (code excerpt of
+ * _fp8_quantize_kernel: widen to fp32, multiply by one reciprocal scale, cast)
+ * with the storage convention of the sglang PR 30971 digest (_quant_q_fp8:
+ * the fp8 tensor holds value / scale; None skips the operation).
+ * Rounding is to nearest, ties to even; magnitudes above 448 (and +-inf)
+ * saturate to +-448; NaN maps to 0x7F with its sign bit.
+ *
+ * x               device, `rows` rows of `cols` elements of dtype `x_dtype`
+ *                 (FP8TS_BF16 or FP8TS_FP16); element (r, c) at x[r * x_row_stride + c]
+ *                 (the 2-D view of any tensor whose leading dims flatten).
+ * out             device, e4m3 bytes; element (r, c) at out[r * out_row_stride + c].
+ * x_row_stride    in elements, >= cols.   out_row_stride in bytes, >= cols.
+ * scale           host, NULL (None) or one finite float > 0.  The reciprocal
+ *                 is computed once on the host in fp32: 1.0f / *scale.
+ * rows == 0 or cols == 0 is a no-op.
+ * Errors: FP8TS_EINVAL for null pointers, negative sizes, short strides, an
+ * unknown dtype, a bad scale, or overlapping x / out.
+ */
+int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
+                 int64_t x_row_stride, uint8_t *out, int64_t out_row_stride,
+                 const float *scale, hipStream_t stream);
+
+/*
+ * indexer_topk - ascending top-k block ids of the lightning indexer.
+ *
+ * Defined by the vLLM PR 45892 digest (implementation steps 1-4 and the
+ * _fmha_indexer_topk excerpt: one maximum score per 128-token tile, tile id =
+ * block id, a [num_index_heads, tokens, topk] shared output buffer) and the
+ * sglang PR 30971 digest (implementation step 2 and review thread 2: strictly
+ * ascending ids, -1 padding when a row has no more than k blocks).
+ *
+ * For query i of sequence b (flattened token t = cu_seqlens_q[b] + i) the
+ * position is p = seq_lens[b] - q_len_b + i; key j is visible iff j <= p.
+ * With nb = p / page_size + 1 visible blocks:
+ *   nb <= topk : ids = 0, 1, ..., nb-1, then -1 ...
+ *   nb >  topk : the topk blocks with the largest
+ *                S[h,t,blk] = max_{j in blk, j <= p} sm_scale*idx_q_scale*idx_k_scale*<iq[t,h], ik[j]>
+ *                (ties to the lower id), written in ascending id order.
+ *
+ * idx_q           device e4m3 [total_q, num_heads, head_dim] contiguous.
+ * idx_k           device e4m3 [num_pages, page_size, head_dim] contiguous (single head).
+ * block_table     device int32 [batch, max_blocks]: logical block -> physical page.
+ * cu_seqlens_q    device int32 [batch + 1], cu_seqlens_q[batch] == total_q.
+ * seq_lens        device int32 [batch], keys of each sequence including this step.
+ * max_q_len       host upper bound of the per-sequence query counts.
+ * num_heads       1, 2, 4, 8 or 16.   head_dim must be 128.   page_size must be 128.
+ * topk            1..64.
+ * out_ids         device int32 [num_heads, total_q, topk].
+ * workspace       device scratch of at least indexer_topk_workspace_size(...) bytes
+ *                 (block scores), 256-byte aligned.
+ * Errors: FP8TS_EINVAL for malformed arguments; FP8TS_EUNSUPPORTED for a head
+ * dim / page size / head count / topk / max_blocks outside the ranges above.
+ */
+size_t indexer_topk_workspace_size(int32_t total_q, int32_t num_heads, int32_t max_blocks);
+
+int indexer_topk(const uint8_t *idx_q, const uint8_t *idx_k, int64_t num_pages,
+                 const int32_t *block_table, int32_t max_blocks,
+                 const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t batch,
+                 int32_t total_q, int32_t max_q_len, int32_t num_heads, int32_t head_dim,
+                 int32_t page_size, float sm_scale, const float *idx_q_scale,
+                 const float *idx_k_scale, int32_t topk, int32_t *out_ids,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sparse_attn_fwd - attention over the selected keys only.
+ *
+ * Semantics (sglang PR 25751 digest, code excerpt of sparse_mla_q8kv8_prefill_fwd,
+ * and sglang PR 30971 digest, summary and implementation step 3):
+ *   s = sm_scale * q_scale                  (q_scale folded into sm_scale)
+ *   z_j = s * k_scale * <q, k_j>            for every selected key j
+ *   z_sink = s * attn_sink[h]               (k_scale never touches the sink)
+ *   M = max(max_j z_j, z_sink);  L = sum_j e^(z_j - M) + e^(z_sink - M)
+ *   out = v_scale * sum_j e^(z_j - M) v_j / L           (bf16; 0 when L == 0)
+ *   lse = M + ln L (natural log, includes the sink; -inf when L == 0)
+ *   max_logits = max_j z_j (keys only; -inf when no key is selected)
+ *
+ * q               device e4m3 [total_q, num_q_heads, head_dim_qk] contiguous.
+ * mode            FP8TS_TOKEN_MODE:
+ *                   k = KV rows [num_kv, head_dim_qk] (one KV head), v = NULL
+ *                   (V = first head_dim_v columns of the same rows, MLA) or
+ *                   [num_kv, head_dim_v]; indices int32 [total_q, topk] token
+ *                   ids (entries outside [0, num_kv) are absent; list order is
+ *                   irrelevant); topk_length NULL or int32 [total_q] (only the
+ *                   first topk_length[t] entries count).  The list is the
+ *                   mask; no causality.  head_dim_qk 576 and head_dim_v 512.
+ *                 FP8TS_BLOCK_MODE:
+ *                   k, v = paged caches [num_kv pages, num_kv_heads, page_size,
+ *                   head_dim]; indices = int32 [num_idx_heads, total_q, topk]
+ *                   block ids as written by indexer_topk (set semantics; -1
+ *                   and ids outside [0, max_blocks) are absent); query head h
+ *                   reads index head h / (Hq / Hidx) and KV head h / (Hq / Hkv);
+ *                   key j of a selected block counts iff j <= p (causal; p as
+ *                   in indexer_topk).  head_dim_qk = head_dim_v = 128,
+ *                   page_size 128.
+ * block_table, cu_seqlens_q, seq_lens, batch, max_q_len: as in indexer_topk
+ *                 (block mode only; may be NULL / 0 in token mode).
+ * attn_sink       device float [num_q_heads] or NULL.
+ * out             device bf16 [total_q, num_q_heads, head_dim_v].
+ * max_logits, lse device float [total_q, num_q_heads].
+ * workspace       device scratch of sparse_attn_workspace_size(...) bytes
+ *                 (may be 0 bytes / NULL when that size is 0).
+ * Errors: FP8TS_EINVAL for malformed arguments; FP8TS_EUNSUPPORTED for head
+ * dims, page sizes or head counts outside the ranges above (a token-mode
+ * head_dim_v other than 512 in particular, as the pages' MLA kernel rejects).
+ */
+size_t sparse_attn_workspace_size(int32_t mode, int32_t batch, int32_t total_q,
+                                  int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t num_idx_heads,
+                                  int32_t head_dim_v, int32_t topk, int32_t max_blocks);
+
+int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v,
+                    int64_t num_kv, const int32_t *indices, int32_t topk,
+                    const int32_t *topk_length, const int32_t *block_table,
+                    int32_t max_blocks, const int32_t *cu_seqlens_q,
+                    const int32_t *seq_lens, int32_t batch, int32_t total_q,
+                    int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t num_idx_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                    int32_t page_size, float sm_scale, const float *q_scale,
+                    const float *k_scale, const float *v_scale, const float *attn_sink,
+                    uint16_t *out, float *max_logits, float *lse, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8TS_H */

@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: exported symbols and host-side validation.
+
+Every call here fails validation (or is an empty no-op) before anything is
+launched, so no kernel runs.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_top_sparse_amd as fts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8ts.h")
+
+EINVAL, EUNSUP = 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fts.LIB_PATH):
+        pytest.skip("libfp8ts.so not built")
+    return fts.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8ts_last_error",
+              "indexer_topk_workspace_size", "sparse_attn_workspace_size", "fp8ts_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in fts.EXPORTED, n
+
+
+def test_abi_version(lib):
+    assert lib.fp8ts_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x100000)
+
+
+def last(lib):
+    return lib.fp8ts_last_error().decode()
+
+
+def sc(v):
+    return ctypes.byref(ctypes.c_float(v))
+
+
+# ----------------------------------------------------------- fp8_quantize
+def q(lib, **kw):
+    a = dict(x=FAKE, dt=0, rows=4, cols=8, xs=8, out=FAKE2, os=8, scale=None)
+    a.update(kw)
+    return lib.fp8_quantize(a["x"], a["dt"], a["rows"], a["cols"], a["xs"], a["out"], a["os"], a["scale"], None)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, dt=2) == EINVAL and "x_dtype" in last(lib)
+    assert q(lib, rows=-1) == EINVAL
+    assert q(lib, scale=sc(-1.0)) == EINVAL and "scale" in last(lib)
+    assert q(lib, scale=sc(0.0)) == EINVAL
+    assert q(lib, scale=sc(float("inf"))) == EINVAL
+    assert q(lib, scale=sc(float("nan"))) == EINVAL
+    assert q(lib, xs=7) == EINVAL and "x_row_stride" in last(lib)
+    assert q(lib, os=4) == EINVAL and "out_row_stride" in last(lib)
+    assert q(lib, x=None) == EINVAL
+    assert q(lib, out=ctypes.c_void_p(0x1000 + 10)) == EINVAL and "overlap" in last(lib)
+    # empty tensors are a no-op that never touches the GPU
+    assert q(lib, rows=0) == 0
+    assert q(lib, cols=0, x=None, out=None) == 0
+
+
+# ----------------------------------------------------------- indexer_topk
+def ix(lib, **kw):
+    a = dict(q=FAKE, k=FAKE2, pages=16, bt=FAKE, mb=16, cu=FAKE, sl=FAKE, B=1, T=100, mq=100, H=4, D=128,
+             page=128, sm=0.1, qs=None, ks=None, topk=8, out=ctypes.c_void_p(0x10000000), ws=FAKE,
+             wsz=1 << 30)
+    a.update(kw)
+    return lib.indexer_topk(a["q"], a["k"], a["pages"], a["bt"], a["mb"], a["cu"], a["sl"], a["B"], a["T"],
+                            a["mq"], a["H"], a["D"], a["page"], a["sm"], a["qs"], a["ks"], a["topk"],
+                            a["out"], a["ws"], a["wsz"], None)
+
+
+def test_indexer_validation(lib):
+    assert ix(lib, D=64) == EUNSUP and "head_dim" in last(lib)
+    assert ix(lib, page=64) == EUNSUP and "page_size" in last(lib)
+    assert ix(lib, H=3) == EUNSUP
+    assert ix(lib, topk=65) == EUNSUP and "topk" in last(lib)
+    assert ix(lib, topk=0) == EUNSUP
+    assert ix(lib, mb=5000) == EUNSUP
+    assert ix(lib, sm=-1.0) == EINVAL
+    assert ix(lib, qs=sc(-2.0)) == EINVAL and "idx_q_scale" in last(lib)
+    assert ix(lib, ks=sc(float("nan"))) == EINVAL and "idx_k_scale" in last(lib)
+    assert ix(lib, ws=None) == EINVAL and "workspace" in last(lib)
+    assert ix(lib, wsz=16) == EINVAL
+    assert ix(lib, ws=ctypes.c_void_p(0x1008)) == EINVAL and "aligned" in last(lib)
+    assert ix(lib, bt=None) == EINVAL
+    assert ix(lib, mq=200) == EINVAL
+    assert ix(lib, T=0) == 0          # nothing to do
+
+
+def test_indexer_workspace_size(lib):
+    assert lib.indexer_topk_workspace_size(1000, 4, 256) == 1000 * 4 * 256 * 4
+    assert lib.indexer_topk_workspace_size(0, 4, 256) == 0
+
+
+# ----------------------------------------------------------- sparse_attn_fwd
+def at(lib, **kw):
+    a = dict(mode=0, q=FAKE, k=FAKE2, v=None, nkv=4096, idx=FAKE, topk=256, tl=None, bt=None, mb=0, cu=None,
+             sl=None, B=0, T=64, mq=0, Hq=16, Hkv=1, Hidx=1, Dqk=576, Dv=512, page=0, sm=1 / 24, qs=None,
+             ks=None, vs=None, sink=None, out=ctypes.c_void_p(0x10000000), ml=FAKE, lse=FAKE, ws=FAKE,
+             wsz=1 << 30)
+    a.update(kw)
+    return lib.sparse_attn_fwd(a["mode"], a["q"], a["k"], a["v"], a["nkv"], a["idx"], a["topk"], a["tl"], a["bt"],
+                               a["mb"], a["cu"], a["sl"], a["B"], a["T"], a["mq"], a["Hq"], a["Hkv"], a["Hidx"],
+                               a["Dqk"], a["Dv"], a["page"], a["sm"], a["qs"], a["ks"], a["vs"], a["sink"],
+                               a["out"], a["ml"], a["lse"], a["ws"], a["wsz"], None)
+
+
+BLOCK = dict(mode=1, v=FAKE2, bt=FAKE, mb=64, cu=FAKE, sl=FAKE, B=1, T=8192, mq=8192, Hq=16, Hkv=2, Hidx=4,
+             Dqk=128, Dv=128, page=128, topk=64, nkv=64)
+
+
+def test_attention_token_mode_validation(lib):
+    assert at(lib, Dv=256) == EUNSUP and "d_v" in last(lib)
+    assert at(lib, Dqk=512) == EUNSUP
+    assert at(lib, Hkv=2, Hq=16) == EUNSUP
+    assert at(lib, mode=7) == EINVAL
+    assert at(lib, sm=float("nan")) == EINVAL
+    assert at(lib, qs=sc(0.0)) == EINVAL and "q_scale" in last(lib)
+    assert at(lib, ks=sc(-1.0)) == EINVAL and "k_scale" in last(lib)
+    assert at(lib, vs=sc(float("inf"))) == EINVAL and "v_scale" in last(lib)
+    assert at(lib, idx=None) == EINVAL
+    assert at(lib, nkv=0) == EINVAL
+    assert at(lib, out=FAKE) == EINVAL and "overlap" in last(lib)
+    assert at(lib, T=0) == 0
+
+
+def test_attention_block_mode_validation(lib):
+    assert at(lib, **{**BLOCK, "page": 64}) == EUNSUP and "page_size" in last(lib)
+    assert at(lib, **{**BLOCK, "Dv": 64}) == EUNSUP
+    assert at(lib, **{**BLOCK, "Hidx": 3}) == EINVAL
+    assert at(lib, **{**BLOCK, "Hq": 24, "Hkv": 4, "Hidx": 6}) == EUNSUP    # groups of 6 and 4 do not nest
+    assert at(lib, **{**BLOCK, "Hq": 12, "Hkv": 2, "Hidx": 3}) == EUNSUP and "nest" in last(lib)
+    assert at(lib, **{**BLOCK, "topk": 65}) == EUNSUP
+    assert at(lib, **{**BLOCK, "mb": 5000}) == EUNSUP
+    assert at(lib, **{**BLOCK, "v": None}) == EINVAL
+    assert at(lib, **{**BLOCK, "bt": None}) == EINVAL
+    assert at(lib, **{**BLOCK, "mq": 9000}) == EINVAL
+    assert at(lib, **{**BLOCK, "Hq": 15}) == EINVAL
+
+
+def test_attention_workspace_sizes(lib):
+    # prefill block mode and large-head token mode need no workspace
+    assert lib.sparse_attn_workspace_size(1, 1, 8192, 8192, 16, 2, 4, 128, 64, 64) == 0
+    assert lib.sparse_attn_workspace_size(0, 0, 4096, 0, 128, 1, 1, 512, 2048, 0) == 0
+    # decode splits the block union: partial O plus (m, l) per split
+    n = lib.sparse_attn_workspace_size(1, 64, 64, 1, 16, 2, 4, 128, 64, 256)
+    assert n > 64 * 16 * 128 * 4
+    # small token mode splits its index list
+    assert lib.sparse_attn_workspace_size(0, 0, 64, 0, 16, 1, 1, 512, 256, 0) > 0
+
+
+# ----------------------------------------------------------- host logic of the binding
+def test_flatten_to_2d():
+    x = torch.empty(4, 3, 8)
+    assert fts.flatten_to_2d(x) == (12, 8, 8)
+    y = torch.empty(4, 3, 16)[..., :8]
+    assert fts.flatten_to_2d(y) == (12, 8, 16)
+    with pytest.raises(ValueError):
+        fts.flatten_to_2d(torch.empty(8, 4).t())
+    with pytest.raises(ValueError):
+        fts.flatten_to_2d(torch.empty(4, 6, 8)[:, :3, :])
+
+
+def test_binding_maps_status_to_python_errors(lib):
+    assert q(lib, dt=9) == EINVAL
+    with pytest.raises(ValueError, match="x_dtype"):
+        fts._check(EINVAL)
+    with pytest.raises(fts.Fp8tsError):
+        fts._check(3)

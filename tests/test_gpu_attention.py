@@ -1,0 +1,299 @@
+"""sparse_attn_fwd on the GPU vs the float64 oracle.
+
+Outputs: max|out - ref| <= 2e-2 * max|ref| per tensor, |lse - ref| <= 1e-3,
+max_logits within 1e-3 * max(1, |ref|); -inf must match -inf.  Bitwise
+checks cover the closed forms the method fixes exactly on the GPU too.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from oracle import e4m3
+from oracle import indexer as OI
+from oracle import quantize as OQ
+import workloads as W
+from helpers import assert_attention_close, bf16_dev, dev, host, workload
+
+pytestmark = pytest.mark.gpu
+PAGE = 128
+TAB = e4m3.decode_table()
+
+
+def rand_codes(rng, shape, std=1.0):
+    return W.e4m3_codes((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+# ------------------------------------------------------------------ token mode
+def token_case(T, Hq, S, topk, seed, sink=True, with_invalid=False):
+    rng = np.random.default_rng(seed)
+    q8 = rand_codes(rng, (T, Hq, 576), 2.0)
+    kv8 = rand_codes(rng, (S, 576))
+    idx = np.stack([rng.choice(S, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    if with_invalid:
+        idx[0, :] = -1                      # a query with no valid key
+        idx[1, ::3] = -1
+        idx[2, 5] = S + 7                   # out of range: absent
+    sk = (rng.standard_normal(Hq) * 3).astype(np.float32) if sink else None
+    return q8, kv8, idx, sk
+
+
+def run_token(gpu, q8, kv8, idx, sm, **kw):
+    sink = kw.pop("attn_sink", None)
+    tl = kw.pop("topk_length", None)
+    return gpu.sparse_attn_fwd(dev(q8), dev(kv8), dev(idx), sm_scale=sm, mode="token", d_v=512,
+                               attn_sink=None if sink is None else dev(sink),
+                               topk_length=None if tl is None else dev(tl), **kw)
+
+
+def test_token_mode_tiny_mla_workload(gpu):
+    wl = workload(1)
+    q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
+    got = run_token(gpu, q8, wl.kv8, wl.indices, wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
+                    v_scale=wl.v_scale, attn_sink=wl.sink)
+    ref = OA.sparse_attn_token(q8, wl.kv8, wl.indices, sm_scale=wl.sm_scale, d_v=512, q_scale=wl.q_scale,
+                               k_scale=wl.k_scale, v_scale=wl.v_scale, attn_sink=wl.sink)
+    assert_attention_close(got, ref, "mla tiny")
+
+
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_token_mode_ragged_and_invalid(gpu, Hq):
+    q8, kv8, idx, sk = token_case(6, Hq, 3000, 300, seed=Hq, with_invalid=True)
+    got = run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=0.7, k_scale=1.3, v_scale=0.9, attn_sink=sk)
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, q_scale=0.7, k_scale=1.3, v_scale=0.9,
+                               attn_sink=sk)
+    assert_attention_close(got, ref, f"token Hq={Hq}")
+
+
+def test_token_mode_topk_length_and_no_sink(gpu):
+    q8, kv8, idx, _ = token_case(5, 16, 2000, 200, seed=3, sink=False)
+    tl = np.array([200, 1, 0, 77, 130], np.int32)
+    got = run_token(gpu, q8, kv8, idx, 1 / 24, topk_length=tl)
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, topk_length=tl)
+    assert_attention_close(got, ref, "topk_length")
+    out, ml, lse = (host(x) for x in got)
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2])) and np.all(np.isneginf(ml[2]))
+
+
+def test_token_mode_separate_v(gpu):
+    q8, kv8, idx, sk = token_case(4, 16, 1000, 96, seed=4)
+    v8 = rand_codes(np.random.default_rng(5), (1000, 512))
+    got = gpu.sparse_attn_fwd(dev(q8), dev(kv8), dev(idx), sm_scale=1 / 24, mode="token", v=dev(v8),
+                              attn_sink=dev(sk))
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, v8=v8, attn_sink=sk)
+    assert_attention_close(got, ref, "separate v")
+
+
+def test_token_mode_long_mla_sampled(gpu):
+    """Full-size long MLA prefill: 4096 x 128 heads, top-2048 of 65536, sink."""
+    wl = workload(4)
+    q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
+    got = run_token(gpu, q8, wl.kv8, wl.indices, wl.sm_scale, attn_sink=wl.sink)
+    rng = np.random.default_rng(2)
+    toks = np.sort(rng.choice(q8.shape[0], 12, replace=False))
+    ref = OA.sparse_attn_token(q8, wl.kv8, wl.indices, sm_scale=wl.sm_scale, d_v=512, attn_sink=wl.sink,
+                               tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "long mla sampled")
+
+
+# ------------------------------------------------------------------ GPU closed forms
+def test_single_key_gives_v_bitwise(gpu):
+    q8, kv8, _, _ = token_case(3, 16, 500, 4, seed=7, sink=False)
+    idx = np.full((3, 4), -1, np.int32)
+    idx[:, 0] = [5, 17, 499]
+    out, ml, lse = (host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, v_scale=2.0))
+    for t, j in enumerate([5, 17, 499]):
+        v = TAB[kv8[j, :512]] * 2.0
+        expect = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(out[t], np.broadcast_to(expect, out[t].shape))
+        # lse = max_logits = z_j, up to fp32 accumulation of the 576-term dot
+        z = (TAB[q8[t]] @ TAB[kv8[j]]) / 24
+        assert np.allclose(lse[t], z, rtol=0, atol=1e-4) and np.allclose(ml[t], z, rtol=0, atol=1e-4)
+
+
+def test_scale_invariants_bitwise(gpu):
+    q8, kv8, idx, sk = token_case(4, 16, 2000, 130, seed=8)
+    base = [host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=0.75, k_scale=1.5, v_scale=1.25,
+                                       attn_sink=sk)]
+    # (q, k, sink) -> (2q, k/2, sink/2): identical bits
+    b2 = [host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=1.5, k_scale=0.75, v_scale=1.25,
+                                     attn_sink=sk / 2)]
+    for x, y in zip(base, b2):
+        assert np.array_equal(x, y)
+    # v_scale doubles out bitwise, leaves lse and max_logits
+    b3 = [host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=0.75, k_scale=1.5, v_scale=2.5,
+                                     attn_sink=sk)]
+    assert np.array_equal(2 * base[0], b3[0])
+    assert np.array_equal(base[1], b3[1]) and np.array_equal(base[2], b3[2])
+    # None == 1.0 bitwise
+    n1 = [host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24)]
+    n2 = [host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=1.0, k_scale=1.0, v_scale=1.0)]
+    for x, y in zip(n1, n2):
+        assert np.array_equal(x, y)
+
+
+def test_k_scale_never_touches_sink_bitwise(gpu):
+    q8, kv8, idx, sk = token_case(3, 16, 1000, 64, seed=9)
+    zk = np.zeros_like(kv8)
+    v8 = kv8[:, :512].copy()
+    a = [host(x) for x in gpu.sparse_attn_fwd(dev(q8), dev(zk), dev(idx), sm_scale=1 / 24, mode="token",
+                                              v=dev(v8), k_scale=0.5, attn_sink=dev(sk))]
+    b = [host(x) for x in gpu.sparse_attn_fwd(dev(q8), dev(zk), dev(idx), sm_scale=1 / 24, mode="token",
+                                              v=dev(v8), k_scale=7.0, attn_sink=dev(sk))]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_sink_only_gives_zero(gpu):
+    q8, kv8, idx, _ = token_case(2, 16, 100, 8, seed=10, sink=False)
+    idx[:] = -1
+    sink = np.linspace(-3, 3, 16).astype(np.float32)
+    out, ml, lse = (host(x) for x in run_token(gpu, q8, kv8, idx, 0.5, q_scale=2.0, attn_sink=sink))
+    assert np.all(out == 0)
+    assert np.allclose(lse, np.broadcast_to(sink * 1.0, lse.shape), atol=1e-6)
+    assert np.all(np.isneginf(ml))
+
+
+# ------------------------------------------------------------------ block mode
+def block_case(seq_lens, q_lens, seed, topk, Hq=16, Hkv=2, Hidx=4, scales=None, sink=False):
+    rng = np.random.default_rng(seed)
+    B = len(seq_lens)
+    nbs = [(s + PAGE - 1) // PAGE for s in seq_lens]
+    max_blocks = max(nbs)
+    P = sum(nbs) + 2
+    perm = rng.permutation(P).astype(np.int32)
+    bt = np.full((B, max_blocks), -1, np.int32)
+    o = 0
+    for b, nb in enumerate(nbs):
+        bt[b, :nb] = perm[o:o + nb]
+        o += nb
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q8 = rand_codes(rng, (T, Hq, 128), 1.5)
+    kc = rand_codes(rng, (P, Hkv, PAGE, 128))
+    vc = rand_codes(rng, (P, Hkv, PAGE, 128))
+    iq = rand_codes(rng, (T, Hidx, 128))
+    ik = rand_codes(rng, (P, PAGE, 128))
+    sl = np.asarray(seq_lens, np.int32)
+    ids = OI.indexer_topk(iq, ik, bt, cu, sl, sm_scale=0.1, topk=topk)     # oracle ids as the input
+    sk = (rng.standard_normal(Hq) * 4).astype(np.float32) if sink else None
+    return dict(q8=q8, kc=kc, vc=vc, ids=ids, bt=bt, cu=cu, sl=sl, mq=max(q_lens), sink=sk)
+
+
+def run_block(gpu, c, sm=0.088, **kw):
+    return gpu.sparse_attn_fwd(dev(c["q8"]), dev(c["kc"]), dev(c["ids"]), v=dev(c["vc"]), sm_scale=sm,
+                               mode="block", block_table=dev(c["bt"]), cu_seqlens_q=dev(c["cu"]),
+                               seq_lens=dev(c["sl"]), max_q_len=c["mq"],
+                               attn_sink=None if c["sink"] is None else dev(c["sink"]), **kw)
+
+
+def ref_block(c, sm=0.088, tokens=None, **kw):
+    return OA.sparse_attn_block(c["q8"], c["kc"], c["vc"], c["ids"], c["bt"], c["cu"], c["sl"], sm_scale=sm,
+                                attn_sink=c["sink"], tokens=tokens, **kw)
+
+
+@pytest.mark.parametrize("topk", [4, 64])
+def test_block_prefill_several_tiles(gpu, topk):
+    c = block_case([2000], [2000], seed=topk, topk=topk)
+    got = run_block(gpu, c, q_scale=0.8, k_scale=1.25, v_scale=0.5)
+    toks = np.arange(0, 2000, 3)
+    ref = ref_block(c, tokens=toks, q_scale=0.8, k_scale=1.25, v_scale=0.5)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, f"block prefill k={topk}")
+
+
+def test_block_varlen_prefix_decode_mix_with_sink(gpu):
+    c = block_case([1700, 900, 5000, 129, 1], [600, 900, 1, 1, 1], seed=11, topk=6, sink=True)
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, "varlen")
+
+
+def test_block_decode_batch(gpu):
+    rng = np.random.default_rng(12)
+    seq = [int(x) for x in rng.integers(1, 12000, 14)] + [1, 128, 129]
+    c = block_case(seq, [1] * len(seq), seed=13, topk=16)
+    got = run_block(gpu, c, v_scale=3.0)
+    ref = ref_block(c, v_scale=3.0)
+    assert_attention_close(got, ref, "decode")
+
+
+def test_block_head_layouts(gpu):
+    # 8 q heads, 8 kv heads (G = 1), 2 index heads (4 q heads each)
+    c = block_case([700], [700], seed=14, topk=3, Hq=8, Hkv=8, Hidx=2)
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, "G=1")
+    # 32 q heads over 1 kv head, 8 index heads
+    c = block_case([900, 300], [900, 50], seed=15, topk=2, Hq=32, Hkv=1, Hidx=8)
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, "G=32")
+
+
+def test_block_rows_with_no_blocks(gpu):
+    c = block_case([600], [600], seed=16, topk=4)
+    c["ids"] = c["ids"].copy()
+    c["ids"][:, 100:110] = -1           # rows that selected nothing
+    c["ids"][1, 300:305, 0] = 99        # id beyond the table: absent
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, "empty rows")
+    out, ml, lse = (host(x) for x in got)
+    assert np.all(out[100:110] == 0) and np.all(np.isneginf(lse[100:110]))
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_block_prefill_full_size_sampled(gpu, n):
+    """8k / 32k causal prefill at full size, ids from the oracle indexer."""
+    wl = workload(n)
+    q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
+    iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
+    T = q8.shape[0]
+    rng = np.random.default_rng(n)
+    toks = np.sort(np.concatenate([rng.choice(T, 10, replace=False), [0, 1, T - 1]]))
+    toks = np.unique(toks)
+    # full id tensor: padding branch rows in closed form, scored rows by the oracle
+    ids = np.empty((4, T, wl.topk), np.int32)
+    nb = np.arange(T) // PAGE + 1
+    ids[:] = np.where(np.arange(wl.topk)[None, :] < nb[:, None], np.arange(wl.topk)[None, :], -1)[None]
+    scored = np.nonzero(nb > wl.topk)[0]
+    if len(scored):
+        # rows that are not sampled keep a valid but arbitrary selection (the first k blocks)
+        ids[:, scored] = np.arange(wl.topk)[None, None, :]
+        need = toks[nb[toks] > wl.topk]
+        if len(need):
+            ids[:, need] = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                                           sm_scale=wl.idx_sm_scale, idx_q_scale=wl.idx_q_scale,
+                                           idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=need)
+    got = gpu.sparse_attn_fwd(dev(q8), dev(wl.k_cache8), dev(ids), v=dev(wl.v_cache8), sm_scale=wl.sm_scale,
+                              mode="block", block_table=dev(wl.block_table), cu_seqlens_q=dev(wl.cu_seqlens_q),
+                              seq_lens=dev(wl.seq_lens), max_q_len=wl.max_q_len, q_scale=wl.q_scale,
+                              k_scale=wl.k_scale, v_scale=wl.v_scale)
+    ref = OA.sparse_attn_block(q8, wl.k_cache8, wl.v_cache8, ids, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                               sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
+                               v_scale=wl.v_scale, tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, f"workload {n}")
+
+
+def test_block_decode_full_size_sampled(gpu):
+    """Decode: 64 sequences x 32k tokens, top-64 blocks per index head."""
+    wl = workload(5)
+    q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
+    iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
+    seqs = [0, 17, 63]
+    ids = np.tile(np.arange(wl.topk, dtype=np.int32), (4, 64, 1))
+    ids[:, seqs] = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                                   sm_scale=wl.idx_sm_scale, topk=wl.topk, tokens=seqs)
+    got = gpu.sparse_attn_fwd(dev(q8), dev(wl.k_cache8), dev(ids), v=dev(wl.v_cache8), sm_scale=wl.sm_scale,
+                              mode="block", block_table=dev(wl.block_table), cu_seqlens_q=dev(wl.cu_seqlens_q),
+                              seq_lens=dev(wl.seq_lens), max_q_len=1)
+    ref = OA.sparse_attn_block(q8, wl.k_cache8, wl.v_cache8, ids, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                               sm_scale=wl.sm_scale, tokens=seqs)
+    out, ml, lse = got
+    assert_attention_close((out[seqs], ml[seqs], lse[seqs]), ref, "decode full")
