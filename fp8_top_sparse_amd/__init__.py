@@ -58,11 +58,15 @@ class Fp8tsError(RuntimeError):
     """A HIP runtime failure reported by the library."""
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfp8ts.so (once).  Raises if it is missing: no fallback exists."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfp8ts.so (once).  Raises if it is missing: no fallback exists.
+
+    ``FP8TS_LIB`` in the environment selects another build of the same library.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("FP8TS_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m fp8_top_sparse_amd.build`")
     lib = ctypes.CDLL(path)

@@ -40,7 +40,16 @@ namespace fp8ts {
 namespace {
 
 constexpr int kPage = 128;
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+#ifndef FP8TS_BLOCK_WAVES
+#define FP8TS_BLOCK_WAVES 8
+#endif
+// block-mode prefill: waves per 256-row workgroup (4 x 64 rows or 8 x 32 rows)
+constexpr int kPrefillWaves = FP8TS_BLOCK_WAVES;
+// A row's probabilities are taken relative to a reference maximum fixed at its
+// first non-empty tile.  A later tile maximum more than kHeadroom above it
+// (log2 units) could overflow fp32, so the workgroup then reruns its key loop
+// once with the exact row maxima it tracked.
+constexpr float kHeadroom = 64.0f;
 
 struct Grid {
   int n_tiles;   // query tiles per sequence (block) / head groups (token)
@@ -67,24 +76,28 @@ __device__ __forceinline__ v8i gload32(const uint8_t *p) {
   return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Stage one 4-key x 16-dim unit of V (e4m3, rows `rows[0..3]`) into V^T (bf16).
-__device__ __forceinline__ void stage_v_unit(uint8_t *vt, int vpitch, int key0, int d0,
-                                             const uint8_t *r0, const uint8_t *r1,
-                                             const uint8_t *r2, const uint8_t *r3) {
-  const v4i w0 = *reinterpret_cast<const v4i *>(r0);
-  const v4i w1 = *reinterpret_cast<const v4i *>(r1);
-  const v4i w2 = *reinterpret_cast<const v4i *>(r2);
-  const v4i w3 = *reinterpret_cast<const v4i *>(r3);
+// V^T tile layout (bf16): row d holds the keys of dimension d.  Keys are
+// grouped in 8-byte units of 4; the unit index is XOR-swizzled with the row's
+// 16-dim group (d / 16), and the row pitch is 8 bytes past a multiple of 256,
+// so that the staging writes (lanes spread over dim groups) and the MFMA
+// operand reads (lanes spread over 16 consecutive rows) hit distinct banks.
+__device__ __forceinline__ int vt_offset(int vpitch, int d, int key4) {
+  return d * vpitch + 8 * (key4 ^ ((d >> 4) & 7));
+}
+
+// Write one 4-key x 16-dim unit of V (e4m3 rows w[0..3], 16 bytes each, keys
+// 4*kg .. 4*kg+3) into V^T.
+__device__ __forceinline__ void stage_v_regs(uint8_t *vt, int vpitch, int kg, int d0, const v4i *w) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {       // dword q covers dims d0 + 4q .. 4q + 3
-    v4bf c0 = e4m3x4_to_bf16(w0[q]);
-    v4bf c1 = e4m3x4_to_bf16(w1[q]);
-    v4bf c2 = e4m3x4_to_bf16(w2[q]);
-    v4bf c3 = e4m3x4_to_bf16(w3[q]);
+    v4bf c0 = e4m3x4_to_bf16(w[0][q]);
+    v4bf c1 = e4m3x4_to_bf16(w[1][q]);
+    v4bf c2 = e4m3x4_to_bf16(w[2][q]);
+    v4bf c3 = e4m3x4_to_bf16(w[3][q]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v4bf col = {c0[j], c1[j], c2[j], c3[j]};
-      *reinterpret_cast<v4bf *>(vt + (d0 + 4 * q + j) * vpitch + 2 * key0) = col;
+      v4bf colv = {c0[j], c1[j], c2[j], c3[j]};
+      *reinterpret_cast<v4bf *>(vt + vt_offset(vpitch, d0 + 4 * q + j, kg)) = colv;
     }
   }
 }
@@ -93,7 +106,8 @@ __device__ __forceinline__ void stage_v_unit(uint8_t *vt, int vpitch, int key0, 
 template <int DQK, int DV, int KT>
 struct Lds {
   static constexpr int KP = DQK + 16;          // K row pitch (bytes)
-  static constexpr int VP = 2 * KT + 16;       // V^T row pitch (bytes)
+  static constexpr int VP = 2 * KT + 8;        // V^T row pitch (bytes), see vt_offset
+  static_assert(KT / 4 >= 8, "the V^T swizzle needs at least 8 key units per row");
   static constexpr int K_BYTES = KT * KP;
   static constexpr int V_BYTES = DV * VP;
   static constexpr int IDX_OFF = K_BYTES + V_BYTES;
@@ -269,30 +283,86 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
 
   // ---------------------------------------------------------------- key tiles
   const int n_iter = BLOCK ? (range_hi - range_lo) : (range_hi - range_lo + KT - 1) / KT;
+
+  // Block mode stages tile it+1 from HBM into registers while tile it is being
+  // computed (one page of one KV head: K and V are 16 KB contiguous each).
+  constexpr int K_CHUNKS = KT * (DQK / 16);            // 16-byte chunks of K
+  constexpr int K_PER = BLOCK ? (K_CHUNKS + NT - 1) / NT : 1;
+  constexpr int V_UNITS = (KT / 4) * (DV / 16);        // 4-key x 16-dim units of V
+  constexpr int V_PER = BLOCK ? (V_UNITS + NT - 1) / NT : 1;
+  v4i kreg[K_PER];
+  v4i vreg[V_PER][4];
+  int cur_page = -1, next_page = -1;
+
+  auto page_of = [&](int it) -> int {
+    const int blk = ulist[range_lo + it];
+    const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
+    return (page >= 0 && page < a.num_kv) ? page : -1;
+  };
+  auto issue_block_loads = [&](int page) {
+    if (page < 0) return;
+    const uint8_t *kp = a.k + ((int64_t)page * a.hkv + kvh) * kPage * DQK;
+    const uint8_t *vp = a.v + ((int64_t)page * a.hkv + kvh) * kPage * DV;
+#pragma unroll
+    for (int j = 0; j < K_PER; ++j) {
+      const int ch = tid + j * NT;
+      if (ch < K_CHUNKS) kreg[j] = *reinterpret_cast<const v4i *>(kp + 16 * ch);
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int u = tid + j * NT;
+      if (u < V_UNITS) {
+        const int kg = u / (DV / 16);
+        const int dg = u - kg * (DV / 16);
+        const uint8_t *r = vp + (4 * kg) * DV + 16 * dg;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vreg[j][q] = *reinterpret_cast<const v4i *>(r + q * DV);
+      }
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+  bool overflow = false;
+  if constexpr (BLOCK) {
+    if (n_iter > 0) {
+      next_page = page_of(0);
+      issue_block_loads(next_page);
+    }
+  }
+
   for (int it = 0; it < n_iter; ++it) {
-    int blk = 0;
     int key_base = 0;        // absolute key position of tile row 0 (block mode)
     int n_valid_keys = KT;
     __syncthreads();         // previous tile fully consumed
     if constexpr (BLOCK) {
-      blk = ulist[range_lo + it];
-      const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
-      if (page < 0 || page >= a.num_kv) continue;   // uniform: no keys from this block
-      key_base = blk * kPage;
-      const uint8_t *kp = a.k + ((int64_t)page * a.hkv + kvh) * kPage * DQK;
-      const uint8_t *vp = a.v + ((int64_t)page * a.hkv + kvh) * kPage * DV;
-      for (int ch = tid; ch < KT * (DQK / 16); ch += NT) {
-        const int key = ch / (DQK / 16);
-        const int part = ch - key * (DQK / 16);
-        *reinterpret_cast<v4i *>(kt_s + key * L::KP + 16 * part) =
-            *reinterpret_cast<const v4i *>(kp + key * DQK + 16 * part);
+      cur_page = next_page;
+      key_base = ulist[range_lo + it] * kPage;
+      if (cur_page >= 0) {
+#pragma unroll
+        for (int j = 0; j < K_PER; ++j) {
+          const int ch = tid + j * NT;
+          if (ch < K_CHUNKS) {
+            const int key = ch / (DQK / 16);
+            const int part = ch - key * (DQK / 16);
+            *reinterpret_cast<v4i *>(kt_s + key * L::KP + 16 * part) = kreg[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < V_PER; ++j) {
+          const int u = tid + j * NT;
+          if (u < V_UNITS) {
+            const int kg = u / (DV / 16);
+            const int dg = u - kg * (DV / 16);
+            stage_v_regs(vt_s, L::VP, kg, 16 * dg, vreg[j]);
+          }
+        }
       }
-      for (int u = tid; u < (KT / 4) * (DV / 16); u += NT) {
-        const int kg = u / (DV / 16);
-        const int dg = u - kg * (DV / 16);
-        const uint8_t *r = vp + (4 * kg) * DV + 16 * dg;
-        stage_v_unit(vt_s, L::VP, 4 * kg, 16 * dg, r, r + DV, r + 2 * DV, r + 3 * DV);
+      __syncthreads();
+      if (it + 1 < n_iter) {
+        next_page = page_of(it + 1);
+        issue_block_loads(next_page);   // in flight during this tile's compute
       }
+      if (cur_page < 0) continue;       // uniform: the block has no keys
     } else {
       const int pos0 = range_lo + it * KT;
       for (int j = tid; j < KT; j += NT) {
@@ -303,9 +373,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
         }
         idx_s[j] = id;
       }
-      __syncthreads();
-      n_valid_keys = 0;
-      for (int j = 0; j < KT; ++j) n_valid_keys += idx_s[j] >= 0;
+      n_valid_keys = __syncthreads_count(tid < KT && idx_s[tid < KT ? tid : 0] >= 0);
       for (int ch = tid; ch < KT * (DQK / 16); ch += NT) {
         const int key = ch / (DQK / 16);
         const int part = ch - key * (DQK / 16);
@@ -317,29 +385,36 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
       for (int u = tid; u < (KT / 4) * (DV / 16); u += NT) {
         const int kg = u / (DV / 16);
         const int dg = u - kg * (DV / 16);
-        const uint8_t *rr[4];
+        v4i rows[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int id = idx_s[4 * kg + q];
           // absent keys read row 0 (any finite bytes); their P is exactly 0
-          rr[q] = a.v + (int64_t)(id >= 0 ? id : 0) * a.v_row_stride + 16 * dg;
+          rows[q] = *reinterpret_cast<const v4i *>(a.v + (int64_t)(id >= 0 ? id : 0) * a.v_row_stride + 16 * dg);
         }
-        stage_v_unit(vt_s, L::VP, 4 * kg, 16 * dg, rr[0], rr[1], rr[2], rr[3]);
+        stage_v_regs(vt_s, L::VP, kg, 16 * dg, rows);
       }
+      __syncthreads();
     }
-    __syncthreads();
 
-    // per-row mask bound for this tile: key position must be <= lim
-    int lim[COLS];
+    // rows taking part in this tile, and their last visible key position
+    bool rsel[COLS];
+    int rp[COLS];
 #pragma unroll
     for (int c = 0; c < COLS; ++c) {
       if constexpr (BLOCK) {
-        const bool sel = row_ok[c] && ((bits[row_li[c] * gr.W + (blk >> 5)] >> (blk & 31)) & 1u);
-        lim[c] = sel ? row_p[c] : -1;
+        const int blk = key_base / kPage;
+        rsel[c] = row_ok[c] && ((bits[row_li[c] * gr.W + (blk >> 5)] >> (blk & 31)) & 1u);
+        rp[c] = row_p[c];
       } else {
-        lim[c] = row_ok[c] ? 0x7fffffff : -1;
+        rsel[c] = row_ok[c];
+        rp[c] = 0x7fffffff;
       }
     }
+    bool any_sel = false;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) any_sel |= rsel[c];
+    if (!__any(any_sel)) continue;      // uniform per wave; no barrier until the next tile
 
 #pragma unroll 1
     for (int koff = 0; koff < KT; koff += 64) {
@@ -365,53 +440,61 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
           }
         }
       }
-      // ---- masks
-      const bool tile_has_invalid = !BLOCK && n_valid_keys < KT;
+      // ---- masks, only where some row of the wave needs one
+      if constexpr (BLOCK) {
+        const int kpos0 = key_base + koff;
+        bool part = false;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+        for (int c = 0; c < COLS; ++c) part |= rsel[c] && rp[c] < kpos0 + 63;
+        if (__any(part)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kl = koff + kt * 16 + 4 * g + i;
-          if constexpr (BLOCK) {
-            const int pos = key_base + kl;
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int c = 0; c < COLS; ++c)
-              if (pos > lim[c]) s[kt][c][i] = -INFINITY;
-          } else {
-            const bool kv_ok = !tile_has_invalid || idx_s[kl] >= 0;
+            for (int i = 0; i < 4; ++i) {
+              const int pos = kpos0 + kt * 16 + 4 * g + i;
 #pragma unroll
-            for (int c = 0; c < COLS; ++c)
-              if (!kv_ok || lim[c] < 0) s[kt][c][i] = -INFINITY;
-          }
+              for (int c = 0; c < COLS; ++c)
+                if (pos > rp[c]) s[kt][c][i] = -INFINITY;
+            }
+        }
+      } else {
+        if (n_valid_keys < KT) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (idx_s[koff + kt * 16 + 4 * g + i] < 0) {
+#pragma unroll
+                for (int c = 0; c < COLS; ++c) s[kt][c][i] = -INFINITY;
+              }
+            }
         }
       }
-      // ---- online softmax (log2 domain, lazy rescale)
-      v8bf pb[COLS][2];
+      // ---- online softmax (log2 domain, fixed per-row reference maximum)
 #pragma unroll
       for (int c = 0; c < COLS; ++c) {
         float smax = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) smax = fmaxf(smax, s[kt][c][i]);
+          smax = fmaxf(fmaxf(smax, fmaxf(s[kt][c][0], s[kt][c][1])), fmaxf(s[kt][c][2], s[kt][c][3]));
         smax = group4_max(smax);
-        const float mt = smax * ck;
+        const float mt = rsel[c] ? smax * ck : -INFINITY;
         m_true[c] = fmaxf(m_true[c], mt);
-        if (mt > m_used[c] + kTau) {
-          const float alpha = exp2f(m_used[c] - mt);
-          lsum[c] *= alpha;
+        m_used[c] = m_used[c] == -INFINITY ? mt : m_used[c];   // O and L are still 0 here
+        overflow |= mt > m_used[c] + kHeadroom;
+      }
+      v8bf pb[COLS][2];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt][c] *= alpha;
-          m_used[c] = mt;
-        }
-        const float msub = m_used[c] == -INFINITY ? 0.f : m_used[c];
+      for (int c = 0; c < COLS; ++c) {
+        // rows not in this tile subtract +inf: every probability is exactly 0
+        const float msub = !rsel[c] ? INFINITY : (m_used[c] == -INFINITY ? 0.f : m_used[c]);
         float p[4][4];
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[kt][i] = exp2f(fmaf(s[kt][c][i], ck, -msub));
+            p[kt][i] = __builtin_amdgcn_exp2f(fmaf(s[kt][c][i], ck, -msub));
             ls += p[kt][i];
           }
         lsum[c] += ls;
@@ -431,9 +514,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const uint8_t *vrow = vt_s + (dt * 16 + col) * L::VP + 2 * (koff + 32 * m + 4 * g);
-          const v4bf lo = *reinterpret_cast<const v4bf *>(vrow);
-          const v4bf hi = *reinterpret_cast<const v4bf *>(vrow + 32);
+          const int u = koff / 4 + 8 * m + g;      // key units {u, u + 4} of this lane group
+          const v4bf lo = *reinterpret_cast<const v4bf *>(vt_s + vt_offset(L::VP, dt * 16 + col, u));
+          const v4bf hi = *reinterpret_cast<const v4bf *>(vt_s + vt_offset(L::VP, dt * 16 + col, u + 4));
           const v8bf va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
           for (int c = 0; c < COLS; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[c][m], o[dt][c]);
@@ -441,6 +524,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
       }
     }
   }
+  // rare second pass: restart from the exact row maxima seen in the first one
+  if (pass == 1 || !__syncthreads_or(overflow)) break;
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    m_used[c] = m_true[c];
+    lsum[c] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  }
+  }  // pass
 
   // ---------------------------------------------------------------- epilogue
 #pragma unroll
@@ -541,8 +634,11 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
     gr.G = hq / hkv;
     gr.gqi = hq / hidx;
     gr.W = (max_blocks + 31) / 32;
-    const bool decode = (int64_t)max_q_len * gr.G <= 16;
-    const int rows = decode ? 16 : 256;
+    // few query rows per sequence (decode): 64-row tiles, every wave loads,
+    // only the waves owning valid rows compute; the block union is split
+    // across workgroups to fill the GPU
+    const bool decode = (int64_t)max_q_len * gr.G <= 64;
+    const int rows = decode ? 64 : 256;
     gr.TT = rows / gr.G;
     if (gr.TT < 1) gr.TT = 1;
     gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
@@ -619,8 +715,9 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
   if (pl.nblocks == 0) return FP8TS_OK;
   int st = FP8TS_OK;
   switch (pl.kind) {
-    case 0: st = launch_k(attn_kernel<128, 128, 4, 4, 128, true>, pl, 256, a, stream); break;
-    case 1: st = launch_k(attn_kernel<128, 128, 1, 1, 128, true>, pl, 64, a, stream); break;
+    case 0: st = launch_k(attn_kernel<128, 128, kPrefillWaves, 16 / kPrefillWaves, 128, true>, pl,
+                          kPrefillWaves * 64, a, stream); break;
+    case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
     case 2: st = launch_k(attn_kernel<576, 512, 8, 1, 64, false>, pl, 512, a, stream); break;
     default: st = launch_k(attn_kernel<576, 512, 1, 1, 64, false>, pl, 64, a, stream); break;
   }
