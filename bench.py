@@ -39,7 +39,50 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain copy of known size, so rocprofv3 FETCH_SIZE / WRITE_SIZE can be scaled."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+
+
+TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md"}
+
+
+def kernel_source_digest() -> str:
+    """sha256 (first 16 hex) of the attention kernel source and its build flags."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("fp8_top_sparse_amd/csrc/attention.hip", "fp8_top_sparse_amd/csrc/device.h",
+              "fp8_top_sparse_amd/build.py"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: int):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel changed since it was taken."""
+    path = TRAFFIC_SUMMARY.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    text = open(os.path.join(ROOT, path)).read()
+    import re
+    dig = re.search(r"first 16 hex\): `([0-9a-f]{16})`", text)
+    val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not dig or not val or dig.group(1) != kernel_source_digest():
+        return None
+    return int(val.group(1))
 
 
 def block_attention_flops(ids: np.ndarray, pos: np.ndarray, hq: int, hidx: int, d_qk: int, d_v: int) -> int:
@@ -56,6 +99,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import fp8_top_sparse_amd as fts
@@ -201,7 +248,8 @@ def main():
         "indexer_topk_GBps": (round(index_bytes / (ms["index"] * 1e-3) / 1e9, 1)
                               if block and ms["index"] else None),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": committed_traffic(args.workload)},
     }
 
     if not args.no_cpu_baseline:
