@@ -33,74 +33,16 @@
 //  * Decode and small token-mode workloads split the key list across
 //    workgroups; partial (O, m, l) go to the workspace and a combine kernel
 //    merges them by log-sum-exp.
-#include "device.h"
-#include "internal.h"
+#include "attn_common.h"
 
 namespace fp8ts {
 namespace {
 
-constexpr int kPage = 128;
 #ifndef FP8TS_BLOCK_WAVES
 #define FP8TS_BLOCK_WAVES 8
 #endif
 // block-mode prefill: waves per 256-row workgroup (4 x 64 rows or 8 x 32 rows)
 constexpr int kPrefillWaves = FP8TS_BLOCK_WAVES;
-// A row's probabilities are taken relative to a reference maximum fixed at its
-// first non-empty tile.  A later tile maximum more than kHeadroom above it
-// (log2 units) could overflow fp32, so the workgroup then reruns its key loop
-// once with the exact row maxima it tracked.
-constexpr float kHeadroom = 64.0f;
-
-struct Grid {
-  int n_tiles;   // query tiles per sequence (block) / head groups (token)
-  int splits;    // key-list splits (1 = write final outputs directly)
-  int G;         // block: q heads per kv head
-  int TT;        // block: tokens per tile
-  int gqi;       // block: q heads per index head
-  int n_il;      // block: index heads per kv head tile
-  int NL;        // block: lists per workgroup
-  int W;         // block: 32-bit words per block bitmap
-  float *part_o;   // [splits, T, Hq, DV]
-  float *part_ml;  // [splits, T, Hq, 4] = (m_used, l, m_true, -)
-};
-
-__device__ __forceinline__ v8i lds_read32(const uint8_t *p) {
-  const v4i *q = reinterpret_cast<const v4i *>(p);
-  v4i lo = q[0], hi = q[1];
-  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-__device__ __forceinline__ v8i gload32(const uint8_t *p) {
-  const v4i *q = reinterpret_cast<const v4i *>(p);
-  v4i lo = q[0], hi = q[1];
-  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// V^T tile layout (bf16): row d holds the keys of dimension d.  Keys are
-// grouped in 8-byte units of 4; the unit index is XOR-swizzled with the row's
-// 16-dim group (d / 16), and the row pitch is 8 bytes past a multiple of 256,
-// so that the staging writes (lanes spread over dim groups) and the MFMA
-// operand reads (lanes spread over 16 consecutive rows) hit distinct banks.
-__device__ __forceinline__ int vt_offset(int vpitch, int d, int key4) {
-  return d * vpitch + 8 * (key4 ^ ((d >> 4) & 7));
-}
-
-// Write one 4-key x 16-dim unit of V (e4m3 rows w[0..3], 16 bytes each, keys
-// 4*kg .. 4*kg+3) into V^T.
-__device__ __forceinline__ void stage_v_regs(uint8_t *vt, int vpitch, int kg, int d0, const v4i *w) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {       // dword q covers dims d0 + 4q .. 4q + 3
-    v4bf c0 = e4m3x4_to_bf16(w[0][q]);
-    v4bf c1 = e4m3x4_to_bf16(w[1][q]);
-    v4bf c2 = e4m3x4_to_bf16(w[2][q]);
-    v4bf c3 = e4m3x4_to_bf16(w[3][q]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4bf colv = {c0[j], c1[j], c2[j], c3[j]};
-      *reinterpret_cast<v4bf *>(vt + vt_offset(vpitch, d0 + 4 * q + j, kg)) = colv;
-    }
-  }
-}
 
 // Dynamic LDS layout sizes.
 template <int DQK, int DV, int KT>
@@ -155,75 +97,26 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
   int range_lo = 0, range_hi = 0;  // positions (union list / index list) of this split
 
   if constexpr (BLOCK) {
-    kvh = bid % a.hkv;
-    bid /= a.hkv;
-    b = bid % a.batch;
-    const int tile = gr.n_tiles - 1 - bid / a.batch;
-    // sequence range, clamped to [0, total_q) whatever the device metadata holds
-    cu0 = min(max(a.cu_seqlens_q[b], 0), a.total_q);
-    q_len = min(max(a.cu_seqlens_q[b + 1] - cu0, 0), a.total_q - cu0);
-    seq_len = a.seq_lens[b];
-    t0 = tile * gr.TT;
-    if (t0 >= q_len) return;
-    const int gi_lo = (kvh * gr.G) / gr.gqi;
+    BlockRows<COLS> br;
+    if (!block_rows<COLS>(a, gr, bid, wave, col, br)) return;
+    b = br.b;
+    kvh = br.kvh;
+    cu0 = br.cu0;
+    q_len = br.q_len;
+    seq_len = br.seq_len;
+    t0 = br.t0;
 #pragma unroll
     for (int c = 0; c < COLS; ++c) {
-      const int r = (wave * COLS + c) * 16 + col;
-      const int tt = t0 + r / gr.G;
-      const int h = kvh * gr.G + r % gr.G;
-      // rows past TT * G (when G does not divide the tile) belong to no token
-      row_ok[c] = (r / gr.G) < gr.TT && tt < q_len;
-      row_t[c] = cu0 + tt;
-      row_h[c] = h;
-      row_p[c] = row_ok[c] ? seq_len - q_len + tt : -1;
-      row_li[c] = row_ok[c] ? (r / gr.G) * gr.n_il + (h / gr.gqi - gi_lo) : 0;
+      row_ok[c] = br.row_ok[c];
+      row_t[c] = br.row_t[c];
+      row_h[c] = br.row_h[c];
+      row_p[c] = br.row_p[c];
+      row_li[c] = br.row_li[c];
     }
     bits = reinterpret_cast<uint32_t *>(smem + L::BASE);
-    uint32_t *ubits = bits + gr.NL * gr.W;
-    ucount = reinterpret_cast<int32_t *>(ubits + gr.W);
+    ucount = reinterpret_cast<int32_t *>(bits + (gr.NL + 1) * gr.W);
     ulist = ucount + 4;
-    for (int w = tid; w < (gr.NL + 1) * gr.W; w += NT) bits[w] = 0u;
-    __syncthreads();
-    const int nsel = gr.NL * a.topk;
-    for (int e = tid; e < nsel; e += NT) {
-      const int li = e / a.topk;
-      const int j = e - li * a.topk;
-      const int tt = t0 + li / gr.n_il;
-      const int gi = gi_lo + li % gr.n_il;
-      if (tt >= q_len) continue;
-      const int p = seq_len - q_len + tt;
-      const int id = a.indices[((int64_t)gi * T + cu0 + tt) * a.topk + j];
-      if (id < 0 || id >= a.max_blocks || (int64_t)id * kPage > p) continue;
-      atomicOr(&bits[li * gr.W + (id >> 5)], 1u << (id & 31));
-      atomicOr(&ubits[id >> 5], 1u << (id & 31));
-    }
-    __syncthreads();
-    // wave 0: exclusive scan of the union words' popcounts, then emit ids ascending
-    if (wave == 0) {
-      int running = 0;
-      for (int w0 = 0; w0 < gr.W; w0 += 64) {
-        const int w = w0 + lane;
-        const uint32_t word = w < gr.W ? ubits[w] : 0u;
-        int cnt = __popc(word);
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          int v = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += v;
-        }
-        int pos = running + incl - cnt;
-        uint32_t m = word;
-        while (m) {
-          const int bit = __ffs(m) - 1;
-          ulist[pos++] = w * 32 + bit;
-          m &= m - 1;
-        }
-        running += __shfl(incl, 63, 64);
-      }
-      if (lane == 0) ucount[0] = running;
-    }
-    __syncthreads();
-    const int U = ucount[0];
+    const int U = block_union<NT>(a, gr, kvh, cu0, q_len, seq_len, t0, bits, ucount, ulist);
     const int chunk = (U + gr.splits - 1) / gr.splits;
     range_lo = min(U, split * chunk);
     range_hi = min(U, range_lo + chunk);
@@ -536,42 +429,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
   }  // pass
 
   // ---------------------------------------------------------------- epilogue
-#pragma unroll
-  for (int c = 0; c < COLS; ++c) {
-    const float l_tot = group4_sum(lsum[c]);
-    if (!row_ok[c]) continue;
-    const int64_t rowidx = (int64_t)row_t[c] * a.hq + row_h[c];
-    if (gr.splits > 1) {
-      float *po = gr.part_o + ((int64_t)split * T * a.hq + rowidx) * DV;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<v4f *>(po + dt * 16 + 4 * g) = o[dt][c];
-      if (g == 0) {
-        float *pm = gr.part_ml + ((int64_t)split * T * a.hq + rowidx) * 4;
-        *reinterpret_cast<v4f *>(pm) = (v4f){m_used[c], l_tot, m_true[c], 0.f};
-      }
-      continue;
-    }
-    const bool has_sink = a.sink != nullptr;
-    const float zs = has_sink ? a.sink_scale_log2 * a.sink[row_h[c]] : -INFINITY;
-    const float M = fmaxf(m_used[c], zs);
-    float Lt = 0.f, fo = 0.f;
-    if (M != -INFINITY) {
-      const float wk = m_used[c] == -INFINITY ? 0.f : exp2f(m_used[c] - M);
-      Lt = l_tot * wk + (has_sink ? exp2f(zs - M) : 0.f);
-      fo = Lt > 0.f ? wk * a.v_scale / Lt : 0.f;
-    }
-    uint16_t *orow = a.out + rowidx * DV;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const v4f x = o[dt][c] * fo;
-      uint2 pk = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
-      *reinterpret_cast<uint2 *>(orow + dt * 16 + 4 * g) = pk;
-    }
-    if (g == 0) {
-      a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
-      a.max_logits[rowidx] = m_true[c] * kLn2;
-    }
-  }
+  attn_epilogue<COLS, NDT>(a, gr, split, g, row_ok, row_t, row_h, o, m_used, m_true, lsum);
 }
 
 // Merge split partials: out = v_scale * sum_s O_s 2^(m_s - M) / L.
@@ -659,8 +517,7 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
       pl.kind = 0;
     }
     pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
-    pl.lds = lds_base<128, 128, 128>() +
-             4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
+    pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
   } else {
     if (hq % 128 == 0) {
       pl.kind = 2;

@@ -30,6 +30,12 @@ namespace {
 constexpr int kPage = 128;
 constexpr int kD = 128;
 
+__device__ __forceinline__ v8i lds_read(const uint8_t *p) {
+  const v4i *q = reinterpret_cast<const v4i *>(p);
+  v4i lo = q[0], hi = q[1];
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 struct SeqInfo {
   int b;       // sequence
   int i;       // query index inside the sequence
@@ -103,6 +109,11 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
     }
     qb[c] = v;
   }
+  int p_min = 0x7fffffff;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+    if (row_p[c] >= 0) p_min = min(p_min, row_p[c]);
+  for (int off = 1; off < 64; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, 64));
 
   const int64_t T = a.total_q;
   for (int blk = split * 4 + wave; blk < nb_tile; blk += 4 * splits) {
@@ -121,22 +132,27 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
         ka[kt] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       const int key0 = blk * kPage;
+      const bool causal = key0 + kPage - 1 > p_min;   // wave-uniform
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
+      for (int c = 0; c < CT; ++c) {
+        v4f acc[8];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mfma_16x16x128_e4m3(ka[kt], qb[c], acc);
-          // acc[i]: key key0 + 16 kt + 4 g + i, row c * 16 + col
-          const int kbase = key0 + kt * 16 + 4 * g;
-          const bool diag = kbase + 3 > row_p[c];
+        for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_16x16x128_e4m3(ka[kt], qb[c], (v4f){0.f, 0.f, 0.f, 0.f});
+        float m = -INFINITY;
+        if (causal) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float s = acc[i];
-            if (diag && kbase + i > row_p[c]) s = -INFINITY;
-            mx[c] = fmaxf(mx[c], s);
-          }
+          for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = key0 + kt * 16 + 4 * g + i > row_p[c] ? -INFINITY : acc[kt][i];
+              m = fmaxf(m, v);
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt)
+            m = fmaxf(fmaxf(m, fmaxf(acc[kt][0], acc[kt][1])), fmaxf(acc[kt][2], acc[kt][3]));
         }
+        mx[c] = m;
       }
     }
 #pragma unroll
@@ -150,19 +166,146 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
   }
 }
 
+// ------------------------------------------------------------ shared-tile score kernel
+// Prefill scoring: 4 waves x 4 column tiles = 256 rows (tokens x heads) share
+// each idx_k page, staged once in LDS; the next page is loaded into registers
+// while the current one is scored.
+constexpr int kSWaves = 4, kSCols = 4, kSRows = kSWaves * kSCols * 16;
+constexpr int kKPitch = kD + 16;
+
+__global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[kPage * kKPitch];
+  constexpr int NT = kSWaves * 64;
+  constexpr int K_PER = kPage * kD / 16 / NT;
+  const int H = a.num_heads;
+  const int TT = kSRows / H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, col = lane & 15;
+
+  const int b = blockIdx.x % a.batch;
+  const int tile = n_tiles - 1 - blockIdx.x / a.batch;        // heavy tiles first
+  const int cu0 = min(max(a.cu_seqlens_q[b], 0), a.total_q);
+  const int q_len = min(max(a.cu_seqlens_q[b + 1] - cu0, 0), a.total_q - cu0);
+  const int t0 = tile * TT;
+  if (t0 >= q_len) return;
+  const int seq_len = a.seq_lens[b];
+  const int p_last = seq_len - q_len + min(q_len, t0 + TT) - 1;
+  if (p_last < 0) return;
+  const int nb_tile = min(p_last / kPage + 1, a.max_blocks);
+  if (nb_tile <= a.topk) return;                 // every row takes the padding branch
+
+  v8i qb[kSCols];
+  int row_p[kSCols], row_t[kSCols], row_h[kSCols];
+  int p_min = 0x7fffffff;
+#pragma unroll
+  for (int c = 0; c < kSCols; ++c) {
+    const int r = (wave * kSCols + c) * 16 + col;
+    const int tt = t0 + r / H;
+    const int h = r % H;
+    row_t[c] = cu0 + tt;
+    row_h[c] = h;
+    row_p[c] = (tt < q_len) ? seq_len - q_len + tt : -1;
+    if (row_p[c] >= 0) p_min = min(p_min, row_p[c]);
+    v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tt < q_len) {
+      const v4i *src = reinterpret_cast<const v4i *>(a.idx_q + ((int64_t)(cu0 + tt) * H + h) * kD + 32 * g);
+      v4i lo = src[0], hi = src[1];
+      v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    qb[c] = v;
+  }
+  // smallest visible position over the wave's rows: blocks ending at or below it need no causal mask
+  for (int off = 1; off < 64; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, 64));
+
+  // pages are prefetched two ahead into two register sets (the loop is
+  // unrolled by two so that each set is named statically)
+  v4i kst0[K_PER], kst1[K_PER];
+  bool valid0 = false, valid1 = false;
+  auto load = [&](int blk, v4i (&kst)[K_PER], bool &valid) __attribute__((always_inline)) {
+    if (blk >= nb_tile) return;
+    const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
+    valid = page >= 0 && page < a.num_pages;
+    const uint8_t *src = a.idx_k + (int64_t)(valid ? page : 0) * kPage * kD;
+#pragma unroll
+    for (int j = 0; j < K_PER; ++j)
+      kst[j] = valid ? *reinterpret_cast<const v4i *>(src + 16 * (tid + j * NT)) : (v4i){0, 0, 0, 0};
+  };
+
+  const int64_t T = a.total_q;
+  auto step = [&](int blk, v4i (&kst)[K_PER], bool &valid) __attribute__((always_inline)) {
+    __syncthreads();
+    const bool cur_valid = valid;
+#pragma unroll
+    for (int j = 0; j < K_PER; ++j) {
+      const int ch = tid + j * NT;
+      *reinterpret_cast<v4i *>(ks + (ch >> 3) * kKPitch + 16 * (ch & 7)) = kst[j];
+    }
+    __syncthreads();
+    load(blk + 2, kst, valid);                   // in flight during the next two pages
+
+    float mx[kSCols];
+#pragma unroll
+    for (int c = 0; c < kSCols; ++c) mx[c] = -INFINITY;
+    if (cur_valid) {
+      const int key0 = blk * kPage;
+      const bool causal = key0 + kPage - 1 > p_min;   // wave-uniform
+      v8i ka[8];
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) ka[kt] = lds_read(ks + (kt * 16 + col) * kKPitch + 32 * g);
+#pragma unroll
+      for (int c = 0; c < kSCols; ++c) {
+        // eight independent MFMAs (distinct accumulators), then the row maximum
+        v4f acc[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_16x16x128_e4m3(ka[kt], qb[c], (v4f){0.f, 0.f, 0.f, 0.f});
+        float m = -INFINITY;
+        if (causal) {
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = key0 + kt * 16 + 4 * g + i > row_p[c] ? -INFINITY : acc[kt][i];
+              m = fmaxf(m, v);
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt)
+            m = fmaxf(fmaxf(m, fmaxf(acc[kt][0], acc[kt][1])), fmaxf(acc[kt][2], acc[kt][3]));
+        }
+        mx[c] = m;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kSCols; ++c) {
+      const float m = group4_max(mx[c]);
+      if (g == 0 && row_p[c] >= 0 && blk <= row_p[c] / kPage)
+        a.scores[((int64_t)row_h[c] * T + row_t[c]) * a.max_blocks + blk] = m * a.sigma;
+    }
+  };
+
+  load(0, kst0, valid0);
+  load(1, kst1, valid1);
+  for (int blk = 0; blk < nb_tile; blk += 2) {
+    step(blk, kst0, valid0);
+    if (blk + 1 < nb_tile) step(blk + 1, kst1, valid1);
+  }
+}
+
 // ------------------------------------------------------------ select kernel
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
-
 // One wave per (head, token) row.  E = score slots per lane (nb <= 64 * E).
+// The k-th largest order-preserving key is found by an 8-bit radix select
+// (four passes over a per-wave 256-bin LDS histogram); ties at that key go to
+// the lower block id; ordered ballot compaction then writes the ids ascending.
 template <int E>
 __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
+  __shared__ int hist_s[4][256];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   const int64_t T = a.total_q;
   if (row >= (int64_t)a.num_heads * T) return;
   const int h = (int)(row / T);
@@ -187,19 +330,50 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     key[e] = id < nb ? order_key(sc[id]) : 0u;
   }
 
-  // Largest threshold thr with count(key >= thr) >= k  (the k-th largest key).
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
+  int *hist = hist_s[wave];
+  uint32_t prefix = 0;          // digits of the k-th largest key decided so far
+  int need = k;                 // how many keys at or below the prefix are still to take
 #pragma unroll
-    for (int e = 0; e < E; ++e) cnt += wave_count(e * 64 + lane < nb && key[e] >= cand);
-    if (cnt >= k) thr = cand;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e * 64 + lane < nb && (key[e] & hmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // lane l owns digits 4l .. 4l+3; count the keys with larger digits
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[lane * 4 + j];
+    const int mine = c[0] + c[1] + c[2] + c[3];
+    int suffix = mine;                               // sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_down(suffix, off, 64);
+      if (lane + off < 64) suffix += v;
+    }
+    int cum = suffix - mine;                         // keys with a digit above 4l+3
+    int digit = -1, above = 0;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (cum < need && cum + c[j] >= need) {     // the one bin where the count crosses `need`
+        digit = lane * 4 + j;
+        above = cum;
+      }
+      cum += c[j];
+    }
+    const uint64_t who = __ballot(digit >= 0);      // exactly one lane holds the digit
+    const int src = __ffsll((unsigned long long)who) - 1;
+    digit = __shfl(digit, src, 64);
+    above = __shfl(above, src, 64);
+    prefix |= (uint32_t)digit << shift;
+    need -= above;
   }
-  int gt = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) gt += wave_count(e * 64 + lane < nb && key[e] > thr);
-  const int need = k - gt;   // how many threshold ties to keep, lowest ids first
+  const uint32_t thr = prefix;   // the k-th largest key; `need` ties at thr are kept
 
   // Ordered compaction: ids visited in ascending order, survivors packed in order.
   int base = 0, ties = 0;
@@ -213,7 +387,8 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     const int tie_rank = ties + __popcll(eqm & below);
     const bool sel = valid && (key[e] > thr || (eq && tie_rank < need));
     const uint64_t selm = __ballot(sel);
-    if (sel) out[base + __popcll(selm & below)] = id;
+    const int pos = base + __popcll(selm & below);
+    if (sel && pos < k) out[pos] = id;     // exactly k survive; the bound only guards malformed input
     base += __popcll(selm);
     ties += __popcll(eqm);
   }
@@ -227,8 +402,9 @@ size_t indexer_workspace_bytes(int32_t total_q, int32_t num_heads, int32_t max_b
 
 int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
   if (a.total_q == 0) return FP8TS_OK;
-  // score kernel: prefill tiles of 128 rows, or a single 16-row tile when few
-  // tokens per sequence (decode), with the blocks split across workgroups.
+  // score kernel: prefill tiles of 256 rows sharing staged pages, or a single
+  // 16-row tile when few tokens per sequence (decode), whose waves stream
+  // their own pages with the blocks split across workgroups.
   const int H = a.num_heads;
   const bool small = (int64_t)a.max_q_len * H <= 16;
   if (small) {
@@ -241,11 +417,11 @@ int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(indexer_score_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a,
                        n_tiles, splits);
   } else {
-    const int TT = 128 / H;
+    const int TT = kSRows / H;
     const int n_tiles = (a.max_q_len + TT - 1) / TT;
     const int64_t grid = (int64_t)a.batch * n_tiles;
-    hipLaunchKernelGGL(indexer_score_kernel<8>, dim3((unsigned)grid), dim3(256), 0, stream, a,
-                       n_tiles, 1);
+    hipLaunchKernelGGL(indexer_score_shared_kernel, dim3((unsigned)grid), dim3(kSWaves * 64), 0, stream, a,
+                       n_tiles);
   }
   int st = check_launch("indexer_topk (score)");
   if (st) return st;
