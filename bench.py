@@ -63,8 +63,8 @@ def kernel_source_digest() -> str:
     """sha256 (first 16 hex) of the attention kernel source and its build flags."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("fp8_top_sparse_amd/csrc/attention.hip", "fp8_top_sparse_amd/csrc/device.h",
-              "fp8_top_sparse_amd/build.py"):
+    for f in ("fp8_top_sparse_amd/csrc/attention_block.hip", "fp8_top_sparse_amd/csrc/attn_common.h",
+              "fp8_top_sparse_amd/csrc/device.h", "fp8_top_sparse_amd/build.py"):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -257,44 +257,51 @@ def main():
     print(json.dumps(result))
 
 
-def cpu_baseline(wl, block: bool) -> dict:
-    """The CPU oracle (float64, numpy) on a bounded sample of the same workload."""
+def cpu_baseline(wl, block: bool, min_seconds: float = 10.0, max_tokens: int = 4096) -> dict:
+    """The CPU oracle (float64, numpy) on a bounded sample of the same workload:
+    batches of randomly chosen query tokens go through quantize, indexer and
+    attention until at least `min_seconds` of work is done.  `cores` is the
+    parallelism the oracle actually achieved (process CPU time / wall time)."""
     import workloads as W  # noqa: F401
     from oracle import attention as OA
     from oracle import indexer as OI
     from oracle import quantize as OQ
 
-    cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
     T = wl.q_bf16.shape[0]
-    n = 6 if block else 4
-    toks = np.sort(rng.choice(T, n, replace=False))
-    t0 = time.perf_counter()
-    q8 = OQ.quantize(wl.q_bf16[toks], OQ.BF16, wl.q_scale)
+    order = rng.permutation(T)[:max_tokens]
+    batch = 8 if block else 2
+    flops, done = 0, 0
+    wall0, cpu0 = time.perf_counter(), time.process_time()
     if block:
-        iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
-        ids = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
-                              sm_scale=wl.idx_sm_scale, idx_q_scale=wl.idx_q_scale,
-                              idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=toks)
-        full_q8 = np.zeros(wl.q_bf16.shape, np.uint8)
-        full_q8[toks] = q8
-        full_ids = np.full((ids.shape[0], T, wl.topk), -1, np.int32)
-        full_ids[:, toks] = ids
-        OA.sparse_attn_block(full_q8, wl.k_cache8, wl.v_cache8, full_ids, wl.block_table, wl.cu_seqlens_q,
-                             wl.seq_lens, sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
-                             v_scale=wl.v_scale, tokens=toks)
+        iq8_all = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
         _, pos = OI.positions(wl.cu_seqlens_q, wl.seq_lens)
-        flops = block_attention_flops(ids, pos[toks], wl.q_bf16.shape[1], ids.shape[0], 128, 128)
-    else:
+    while done < len(order) and time.perf_counter() - wall0 < min_seconds:
+        toks = np.sort(order[done:done + batch])
+        done += len(toks)
+        q8 = OQ.quantize(wl.q_bf16[toks], OQ.BF16, wl.q_scale)
         full_q8 = np.zeros(wl.q_bf16.shape, np.uint8)
         full_q8[toks] = q8
-        OA.sparse_attn_token(full_q8, wl.kv8, wl.indices, sm_scale=wl.sm_scale, d_v=wl.d_v, q_scale=wl.q_scale,
-                             k_scale=wl.k_scale, v_scale=wl.v_scale, attn_sink=wl.sink, tokens=toks)
-        flops = int((wl.indices[toks] >= 0).sum()) * wl.q_bf16.shape[1] * 2 * (576 + wl.d_v)
-    dt = time.perf_counter() - t0
+        if block:
+            ids = OI.indexer_topk(iq8_all, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                                  sm_scale=wl.idx_sm_scale, idx_q_scale=wl.idx_q_scale,
+                                  idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=toks)
+            full_ids = np.full((ids.shape[0], T, wl.topk), -1, np.int32)
+            full_ids[:, toks] = ids
+            OA.sparse_attn_block(full_q8, wl.k_cache8, wl.v_cache8, full_ids, wl.block_table, wl.cu_seqlens_q,
+                                 wl.seq_lens, sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
+                                 v_scale=wl.v_scale, tokens=toks)
+            flops += block_attention_flops(ids, pos[toks], wl.q_bf16.shape[1], ids.shape[0], 128, 128)
+        else:
+            OA.sparse_attn_token(full_q8, wl.kv8, wl.indices, sm_scale=wl.sm_scale, d_v=wl.d_v,
+                                 q_scale=wl.q_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                                 attn_sink=wl.sink, tokens=toks)
+            flops += int((wl.indices[toks] >= 0).sum()) * wl.q_bf16.shape[1] * 2 * (576 + wl.d_v)
+    dt = time.perf_counter() - wall0
+    cores = max(1, round((time.process_time() - cpu0) / dt))
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} query tokens of {wl.name} through quantize, indexer and attention "
-                      f"(float64 numpy, {dt:.1f} s)"}
+            "sample": f"{done} query tokens of {wl.name} (random, all heads) through quantize, indexer and "
+                      f"attention (float64 numpy, {dt:.1f} s)"}
 
 
 if __name__ == "__main__":

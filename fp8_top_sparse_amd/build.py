@@ -35,6 +35,7 @@ COMMON_FLAGS = [
 # signalling-NaN canonicalisation that IEEE mode requires
 FILE_FLAGS = {
     "attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attention_block.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

@@ -473,7 +473,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
 
 // ---------------------------------------------------------------- host side
 struct Plan {
-  int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads
+  int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads,
+              // 4 block prefill, double-buffered
   Grid gr;
   int64_t nblocks;
   size_t lds;
@@ -496,7 +497,7 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
     // only the waves owning valid rows compute; the block union is split
     // across workgroups to fill the GPU
     const bool decode = (int64_t)max_q_len * gr.G <= 64;
-    const int rows = decode ? 64 : 256;
+    const int rows = decode ? 64 : block_prefill_rows();
     gr.TT = rows / gr.G;
     if (gr.TT < 1) gr.TT = 1;
     gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
@@ -518,6 +519,20 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
     }
     pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
     pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
+    // prefill tiles go to the pipelined kernel when its LDS fits; otherwise to
+    // the single-buffered one, whose tiles are 256 rows
+    if (pl.kind == 0) {
+      if (block_prefill_lds(gr) <= kMaxLds) {
+        pl.kind = 4;
+        pl.lds = block_prefill_lds(gr);
+      } else if (gr.TT != 256 / gr.G) {
+        gr.TT = 256 / gr.G > 0 ? 256 / gr.G : 1;
+        gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
+        gr.NL = gr.TT * gr.n_il;
+        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+        pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
+      }
+    }
   } else {
     if (hq % 128 == 0) {
       pl.kind = 2;
@@ -543,6 +558,9 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
 
 template <typename K>
 int launch_k(K kern, const Plan &pl, int threads, const AttnArgs &a, hipStream_t stream) {
+  if (pl.lds > kMaxLds)
+    return fail(FP8TS_EUNSUPPORTED, "sparse_attn_fwd: block lists need %zu bytes of LDS (limit %zu); "
+                "use fewer blocks per sequence or more q heads per kv head", pl.lds, kMaxLds);
   if (pl.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
@@ -575,6 +593,7 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
     case 0: st = launch_k(attn_kernel<128, 128, kPrefillWaves, 16 / kPrefillWaves, 128, true>, pl,
                           kPrefillWaves * 64, a, stream); break;
     case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
+    case 4: st = launch_block_prefill(a, pl.gr, pl.nblocks, stream); break;
     case 2: st = launch_k(attn_kernel<576, 512, 8, 1, 64, false>, pl, 512, a, stream); break;
     default: st = launch_k(attn_kernel<576, 512, 1, 1, 64, false>, pl, 64, a, stream); break;
   }

@@ -1,0 +1,437 @@
+// Block-sparse prefill attention for GQA (d_qk = d_v = 128, 128-token pages):
+// the dense-tile kernel behind sparse_attn_fwd in block mode when every
+// sequence has many query rows per KV head.
+//
+// Semantics: sglang PR 25751 digest (sparse attention forward: out bf16,
+// max_logits and lse fp32 per (token, head), optional attn_sink) with block
+// selection as in vLLM PR 45892 digest (each query token attends to the
+// 128-token blocks its index head selected, causally masked), and the scale
+// handling of sglang PR 30971 digest, implementation step 3 (q_scale folded
+// into sm_scale, k_scale on the QK dot only, v_scale on the output).
+//
+// Workgroup: kRows query rows = a tile of consecutive tokens x the q heads of
+// one KV head, split into 16-row column tiles over the waves.  The
+// workgroup walks the ascending union of its rows' block lists; rows that did
+// not select the current block get probability 0.
+//
+// Cost model this layout follows (gfx950, per SIMD): MFMA time and VALU time
+// add up, a wave64 VOP1/VOP2 op issues in ~2 cycles, a VOP3 op in ~4, and
+// v_exp_f32 in ~8.  So the softmax is kept to one VOP2 multiply, one exp, one
+// max, one add and half a bf16 pack per score:
+//  * S^T = K Q^T (+ C) on 16x16x128 e4m3 MFMA, where C holds minus the row's
+//    reference maximum (raw dot units), so p = exp2(ck * S) needs no subtract.
+//    The reference is the row's first tile maximum; a later tile maximum more
+//    than kHeadroom (log2 units) above it makes the workgroup rerun once with
+//    the exact maxima.
+//  * P stays in registers: the S^T output layout of a 16-key tile pair is the
+//    B-operand layout of the 16x16x32 bf16 PV MFMA.
+//  * K (e4m3) and V^T (bf16, keys of every 32-key chunk in PV operand order)
+//    are stored in LDS in MFMA operand order, so each operand fetch is one
+//    contiguous 1 KB wave read.  The staging writes are spread over distinct
+//    bank groups (K: 16 keys per write instruction; V: each thread's dims are
+//    rotated with one v_alignbyte per loaded dword).
+//  * K/V tiles are double-buffered in LDS (or single-buffered, so that two
+//    128-row workgroups share a CU): tile t+1 is written from registers while
+//    tile t is computed and tile t+2 is in flight from HBM.  Barriers order
+//    LDS only, so the prefetch stays in flight across them.
+#include "attn_common.h"
+
+namespace fp8ts {
+namespace {
+
+#ifndef FP8TS_PREFILL_ROWS
+#define FP8TS_PREFILL_ROWS 256
+#endif
+#ifndef FP8TS_PREFILL_BUFS
+#define FP8TS_PREFILL_BUFS 2
+#endif
+constexpr int kD = 128;
+constexpr int kRows = FP8TS_PREFILL_ROWS;  // query rows per workgroup
+constexpr int kBufs = FP8TS_PREFILL_BUFS;  // K/V tile buffers in LDS (2: one barrier per tile)
+constexpr int kNdt = kD / 16;             // 16-dim output tiles
+// K and V^T tiles are stored in MFMA operand order: every operand fetch is
+// one contiguous 1 KB wave read (64 lanes x 16 bytes), which the LDS serves
+// without bank conflicts (padded row layouts cost two passes per read).
+//   K:   operand (kt, hh) of lane l at 1024 * (2 * kt + hh) + 16 * l: key
+//        16 kt + (l & 15), bytes 32 (l >> 4) + 16 hh .. + 15
+//   V^T: operand (dt, m) of lane l at 1024 * (4 * dt + m) + 16 * l: dim
+//        16 dt + (l & 15), keys of chunk 4 m + (l >> 4) (bf16, order vt_key)
+constexpr int kKBytes = kPage * kD;
+constexpr int kVBytes = kD * kPage * 2;
+constexpr int kBufBytes = kKBytes + kVBytes;
+constexpr int kMetaOff = kBufs * kBufBytes;
+constexpr int kKChunks = kPage * kD / 16;           // 16-byte chunks of a K tile
+constexpr int kVUnits = (kD / 4) * 16 * 2;          // 4-dim x 4-key units of a V tile
+
+#ifndef FP8TS_PREFILL_WAVES
+#define FP8TS_PREFILL_WAVES 16
+#endif
+constexpr int kWaves = FP8TS_PREFILL_WAVES;         // 16: 16 rows per wave, 8: 32 rows per wave
+constexpr int kThreads = kWaves * 64;
+constexpr int kCols = kRows / 16 / kWaves;          // 16-row column tiles per wave
+static_assert(kCols * 16 * kWaves == kRows && kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "tile");
+// single-buffered workgroups are sized so that two share a CU
+constexpr int kWavesPerSimd = (kBufs == 1 ? 2 : 1) * kWaves / 4;
+
+// Tile-relative key held in slot j (0..7) of 16-byte V^T chunk cix (0..15):
+// chunk cix = 4 * m + g serves the PV MFMA of 32-key group m for lane group g,
+// whose slots j < 4 are keys 4g + j of the even 16-key S^T tile and slots
+// j >= 4 keys 4g + j - 4 of the odd one.
+__device__ __forceinline__ int vt_key(int cix, int j) {
+  return 32 * (cix >> 2) + 16 * (j >> 2) + 4 * (cix & 3) + (j & 3);
+}
+
+// K staging chunk ch (0..1023, 16 bytes each): wave-instruction q = ch >> 6
+// covers bytes 64 (q & 1) .. + 63 of keys 16 (q >> 1) .. + 15, so that its
+// 16-lane write groups land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int k_chunk_key(int ch) { return 16 * (ch >> 7) + (ch & 15); }
+__device__ __forceinline__ int k_chunk_part(int ch) { return 4 * ((ch >> 6) & 1) + ((ch >> 4) & 3); }
+
+// Two 16-byte reads 1 KB apart (the two halves of a 32-byte K operand).
+__device__ __forceinline__ v8i lds_read32x2(const uint8_t *p) {
+  const v4i lo = *reinterpret_cast<const v4i *>(p);
+  const v4i hi = *reinterpret_cast<const v4i *>(p + 1024);
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ uint32_t bf16x2_from_e4m3(uint32_t packed, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
+}
+
+// Max over the four lane groups (l, l ^ 16, l ^ 32, l ^ 48) holding one MFMA
+// column, with gfx950 row-swap permutes instead of LDS-routed shuffles.  The
+// swaps are written as asm (with the two wait states they need on either
+// side) so that the compiler cannot merge the two halves of a swap.
+__device__ __forceinline__ float group4_max_swap(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+// Raw buffer resource over one 16 KB K or V tile (dword 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const uint8_t *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, kPage * kD, 0x00020000);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
+void attn_block_prefill_kernel(AttnArgs a, Grid gr) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+
+  int bid = blockIdx.x;
+  const int split = bid % gr.splits;
+  bid /= gr.splits;
+  BlockRows<kCols> br;
+  if (!block_rows<kCols>(a, gr, bid, wave, col, br)) return;
+
+  uint32_t *bits = reinterpret_cast<uint32_t *>(smem + kMetaOff);
+  int32_t *ucount = reinterpret_cast<int32_t *>(bits + (gr.NL + 1) * gr.W);
+  int32_t *ulist = ucount + 4;
+  int32_t *plist = ulist + gr.W * 32;
+  const int U = block_union<kThreads>(a, gr, br.kvh, br.cu0, br.q_len, br.seq_len, br.t0, bits, ucount, ulist);
+  const int chunk = (U + gr.splits - 1) / gr.splits;
+  const int lo = min(U, split * chunk);
+  const int n_iter = min(U, lo + chunk) - lo;
+  // physical page of every block this workgroup visits (-1: no such page)
+  for (int i = tid; i < n_iter; i += kThreads) {
+    const int page = a.block_table[(int64_t)br.b * a.max_blocks + ulist[lo + i]];
+    plist[i] = (page >= 0 && page < a.num_kv) ? page : -1;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- Q operands
+  v8i qb[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) {
+    const int64_t qr = br.row_ok[c] ? (int64_t)br.row_t[c] * a.hq + br.row_h[c] : 0;
+    qb[c] = br.row_ok[c] ? gload32(a.q + qr * kD + 32 * g) : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  // ---------------------------------------------------------------- staging
+  // K: 16-byte chunks, row-major.  V: units of 4 dims x 4 keys (half of a
+  // V^T chunk): unit u -> half jh = u & 1, dims 4 * d4 .. + 3 with
+  // d4 = (u >> 1) & 31, chunk cix = u >> 6.
+  constexpr int K_PER = kKChunks / kThreads;
+  constexpr int V_PER = kVUnits / kThreads;
+  const int64_t kv_head_stride = (int64_t)kPage * kD;
+  const int kvh_s = __builtin_amdgcn_readfirstlane(br.kvh);
+  v4i kreg[K_PER];
+  uint32_t vreg[V_PER][4];
+  // page ids are workgroup-uniform: each tile is read through buffer
+  // resources (scalar base, 16 KB extent) with 32-bit lane offsets, so no
+  // 64-bit per-lane address stays live across the loop
+  auto load_tile = [&](int page) {
+    page = __builtin_amdgcn_readfirstlane(page);
+    if (page < 0) return;
+    const int64_t off = ((int64_t)page * a.hkv + kvh_s) * kv_head_stride;
+    const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.k + off);
+    const __amdgpu_buffer_rsrc_t rv = make_tile_rsrc(a.v + off);
+#pragma unroll
+    for (int j = 0; j < K_PER; ++j)
+      kreg[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+          rk, k_chunk_key(tid + j * kThreads) * kD + 16 * k_chunk_part(tid + j * kThreads), 0, 0));
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int u = tid + j * kThreads;
+      const int jh = u & 1, d4 = (u >> 1) & 31, cix = u >> 6;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vreg[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vt_key(cix, 4 * jh + i) * kD + 4 * d4, 0, 0);
+    }
+  };
+  auto store_tile = [&](int page, uint8_t *buf) {
+    if (__builtin_amdgcn_readfirstlane(page) < 0) return;
+#pragma unroll
+    for (int j = 0; j < K_PER; ++j) {
+      const int ch = tid + j * kThreads;
+      const int key = k_chunk_key(ch), part = k_chunk_part(ch);
+      *reinterpret_cast<v4i *>(buf + 1024 * (2 * (key >> 4) + (part & 1)) + 16 * (16 * (part >> 1) + (key & 15))) =
+          kreg[j];
+    }
+    uint8_t *vt = buf + kKBytes;
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int u = tid + j * kThreads;
+      const int jh = u & 1, d4 = (u >> 1) & 31, cix = u >> 6;
+      // rotate so that byte s of w[i] is dim 4 * d4 + ((s + rot) & 3): the
+      // 16 lanes sharing a write cycle then hit 16 distinct bank groups
+      const int rot = (d4 >> 2) & 3;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbyte(vreg[j][i], vreg[j][i], rot);
+      // 4x4 byte transpose: x[s] = byte s of keys 0..3
+      const uint32_t t0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+      const uint32_t t1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+      const uint32_t t2 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+      const uint32_t t3 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+      const uint32_t x[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                             __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int d = 4 * d4 + ((s4 + rot) & 3);
+        const v2i pr = {(int)bf16x2_from_e4m3(x[s4], false), (int)bf16x2_from_e4m3(x[s4], true)};
+        *reinterpret_cast<v2i *>(vt + 1024 * (4 * (d >> 4) + (cix >> 2)) + 16 * (16 * (cix & 3) + (d & 15)) + 8 * jh) = pr;
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- state
+  v4f o[kNdt][kCols];
+  float negm[kCols];      // minus the reference maximum (raw dot units); 0 before the first tile
+  float mraw[kCols];      // exact running maximum (raw dot units)
+  float lsum[kCols];
+  bool started[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) {
+#pragma unroll
+    for (int dt = 0; dt < kNdt; ++dt) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+    negm[c] = 0.f;
+    mraw[c] = -INFINITY;
+    lsum[c] = 0.f;
+    started[c] = false;
+  }
+  const float ck = a.key_scale_log2;
+  const int op_lane = 16 * lane;                       // operand fetch offset of this lane
+
+  // metadata of the tile about to be computed, read one tile ahead
+  int t_blk = 0;
+  bool t_sel[kCols];
+  auto fetch_meta = [&](int it) {
+    t_blk = __builtin_amdgcn_readfirstlane(ulist[lo + it]);
+    const bool has_page = __builtin_amdgcn_readfirstlane(plist[it]) >= 0;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c)
+      t_sel[c] = has_page && br.row_ok[c] && ((bits[br.row_li[c] * gr.W + (t_blk >> 5)] >> (t_blk & 31)) & 1u);
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+    bool overflow = false;
+    if (n_iter > 0) {
+      load_tile(plist[0]);
+      store_tile(plist[0], smem);
+      fetch_meta(0);
+    }
+    if (n_iter > 1) load_tile(plist[1]);
+    // drain the prologue loads here, once: otherwise the wait-count analysis
+    // makes the first MFMA of every tile wait for the in-flight prefetch
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    for (int it = 0; it < n_iter; ++it) {
+      // tile it is in LDS (two buffers: and every wave is done with tile it - 1)
+      lds_barrier();
+      const uint8_t *kt_s = smem + (kBufs == 2 ? (it & 1) * kBufBytes : 0);
+      const uint8_t *vt_s = kt_s + kKBytes;
+      const int blk = t_blk;
+      bool rsel[kCols];
+      bool any_sel = false;
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        rsel[c] = t_sel[c];
+        any_sel |= rsel[c];
+      }
+      // stage tile it + 1 (loaded during the previous tile) into the buffer
+      // tile it - 1 used, and start loading tile it + 2: this VALU and LDS
+      // work overlaps the previous tile's PV products still in the MFMA pipe
+      if (kBufs == 2 && it + 1 < n_iter) {
+        store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
+        if (it + 2 < n_iter) load_tile(plist[it + 2]);
+      }
+      if (__any(any_sel)) {
+        const int key_base = blk * kPage;
+        v4f cinit[kCols];
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+          const float cv = rsel[c] ? negm[c] : -INFINITY;
+          cinit[c] = (v4f){cv, cv, cv, cv};
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // ---- S^T = K Q^T + C for 64 keys
+          v4f s[4][kCols];
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const v8i ka = lds_read32x2(kt_s + op_lane + 1024 * (2 * (4 * h + kt)));
+#pragma unroll
+            for (int c = 0; c < kCols; ++c) s[kt][c] = mfma_16x16x128_e4m3(ka, qb[c], cinit[c]);
+          }
+          // ---- causal mask, only where some row of the wave needs one
+          const int kpos0 = key_base + 64 * h;
+          bool part = false;
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) part |= rsel[c] && br.row_p[c] < kpos0 + 63;
+          if (__any(part)) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int pos = kpos0 + kt * 16 + 4 * g + i;
+#pragma unroll
+                for (int c = 0; c < kCols; ++c)
+                  if (pos > br.row_p[c]) s[kt][c][i] = -INFINITY;
+              }
+          }
+          // ---- row maxima (S units), first-tile references, overflow check
+          float mx[kCols];
+          bool need_start = false;
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+              m = fmaxf(fmaxf(m, fmaxf(s[kt][c][0], s[kt][c][1])), fmaxf(s[kt][c][2], s[kt][c][3]));
+            mx[c] = group4_max_swap(m);
+            if (rsel[c]) mraw[c] = fmaxf(mraw[c], mx[c] - negm[c]);
+            need_start |= rsel[c] && !started[c];
+          }
+          if (__any(need_start)) {
+            // rows selecting their first block take this half's maximum as the
+            // reference (half 0 of a selected block always holds a visible key)
+#pragma unroll
+            for (int c = 0; c < kCols; ++c) {
+              const bool st = rsel[c] && !started[c];
+              const float delta = st ? mx[c] : 0.f;
+#pragma unroll
+              for (int kt = 0; kt < 4; ++kt) s[kt][c] -= delta;
+              mx[c] -= delta;
+              negm[c] -= delta;
+              started[c] = started[c] || st;
+              const float cv = rsel[c] ? negm[c] : -INFINITY;
+              cinit[c] = (v4f){cv, cv, cv, cv};
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) overflow |= mx[c] * ck > kHeadroom;
+          // ---- probabilities, row sums, bf16 B operands
+          v8bf pb[2][kCols];
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) {
+            float p[4][4];
+            float ls = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                p[kt][i] = __builtin_amdgcn_exp2f(s[kt][c][i] * ck);
+                ls += p[kt][i];
+              }
+            lsum[c] += ls;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              v8bf v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                v[i] = (__bf16)p[2 * m][i];
+                v[4 + i] = (__bf16)p[2 * m + 1][i];
+              }
+              pb[m][c] = v;
+            }
+          }
+          // ---- O^T += V^T P^T
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int dt = 0; dt < kNdt; ++dt) {
+              const v8bf va = *reinterpret_cast<const v8bf *>(vt_s + op_lane + 1024 * (4 * dt + 2 * h + m));
+#pragma unroll
+              for (int c = 0; c < kCols; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[m][c], o[dt][c]);
+            }
+          }
+        }
+      }
+      if (it + 1 < n_iter) {
+        fetch_meta(it + 1);
+        if (kBufs == 1) {
+          lds_barrier();     // every wave is done with tile it
+          store_tile(plist[it + 1], smem);
+          if (it + 2 < n_iter) load_tile(plist[it + 2]);
+        }
+      }
+    }
+    // rare second pass: restart from the exact row maxima seen in the first one
+    if (pass == 1 || !__syncthreads_or(overflow)) break;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      started[c] = mraw[c] != -INFINITY;
+      negm[c] = started[c] ? -mraw[c] : 0.f;
+      lsum[c] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < kNdt; ++dt) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  float m_ref[kCols], m_true[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) {
+    m_ref[c] = started[c] ? -negm[c] * ck : -INFINITY;
+    m_true[c] = mraw[c] * ck;
+  }
+  attn_epilogue<kCols, kNdt>(a, gr, split, g, br.row_ok, br.row_t, br.row_h, o, m_ref, m_true, lsum);
+}
+
+}  // namespace
+
+size_t block_prefill_lds(const Grid &gr) {
+  return (size_t)kMetaOff + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + 2 * (size_t)gr.W * 32);
+}
+
+int block_prefill_rows() { return kWaves * kCols * 16; }
+
+int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
+  const size_t lds = block_prefill_lds(gr);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_block_prefill_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return fail(FP8TS_EHIP, "sparse_attn_fwd: LDS attribute: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(attn_block_prefill_kernel, dim3((unsigned)nblocks), dim3(kThreads), lds, stream, a, gr);
+  return check_launch("sparse_attn_fwd (block prefill)");
+}
+
+}  // namespace fp8ts

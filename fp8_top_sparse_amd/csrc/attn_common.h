@@ -35,6 +35,15 @@ struct Grid {
   float *part_ml;  // [splits, T, Hq, 4] = (m_ref, l, m_true, -)
 };
 
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads it
+// does not wait for outstanding global loads, so a tile prefetch issued before
+// it stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ v8i lds_read32(const uint8_t *p) {
   const v4i *q = reinterpret_cast<const v4i *>(p);
   v4i lo = q[0], hi = q[1];
@@ -217,5 +226,11 @@ __device__ __forceinline__ void attn_epilogue(const AttnArgs &a, const Grid &gr,
     }
   }
 }
+
+// Block-mode prefill kernel with double-buffered K/V tiles (attention_block.hip).
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+size_t block_prefill_lds(const Grid &gr);
+int block_prefill_rows();
+int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 
 }  // namespace fp8ts

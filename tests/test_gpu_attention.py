@@ -247,6 +247,31 @@ def test_block_rows_with_no_blocks(gpu):
     assert np.all(out[100:110] == 0) and np.all(np.isneginf(lse[100:110]))
 
 
+def test_block_prefill_late_large_logits(gpu):
+    """Rows whose first blocks carry tiny logits and a later block logits far
+    above them (beyond what fp32 can hold relative to the first reference):
+    the kernel must rescan with the exact row maxima.  The late block's keys
+    have one non-zero coordinate, so its dots are single exact products: the
+    fp8 MFMA accumulates with ~16 bits relative to the largest addend, which
+    would otherwise blur logits in the hundreds by more than the lse bound."""
+    c = block_case([900], [900], seed=17, topk=7)
+    rng = np.random.default_rng(17)
+    kc = c["kc"].copy()
+    bt = c["bt"][0]
+    kc[bt[:3]] = rand_codes(rng, (3,) + kc.shape[1:], 0.02)
+    kc[bt[4]] = 0
+    kc[bt[4], :, :, 0] = W.e4m3_codes(rng.uniform(256, 448, kc.shape[1:3]).astype(np.float32))
+    c["kc"] = kc
+    nb = np.arange(900) // PAGE + 1
+    ids = np.where(np.arange(7)[None, :] < nb[:, None], np.arange(7)[None, :], -1).astype(np.int32)
+    c["ids"] = np.broadcast_to(ids[None], (4, 900, 7)).copy()
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    ml = ref[2]
+    assert ml[PAGE * 4:].max() - ml[:PAGE * 3].max() > 64 * math.log(2)   # the case is really exercised
+    assert_attention_close(got, ref, "late large logits")
+
+
 @pytest.mark.parametrize("n", [2, 3])
 def test_block_prefill_full_size_sampled(gpu, n):
     """8k / 32k causal prefill at full size, ids from the oracle indexer."""
