@@ -30,12 +30,16 @@ COMMON_FLAGS = [
 ]
 
 
-# per-file flags: the attention kernels never test for NaN (NaN inputs give
-# unspecified outputs there), which lets fmaxf map to v_max3 without the
-# signalling-NaN canonicalisation that IEEE mode requires
+# per-file flags: the attention and indexer kernels never test for NaN (NaN
+# inputs give unspecified outputs there), which lets fmaxf map to v_max3
+# without the signalling-NaN canonicalisation that IEEE mode requires
+NO_NAN = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 FILE_FLAGS = {
-    "attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-    "attention_block.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "attention.hip": NO_NAN,
+    "attention_block.hip": NO_NAN,
+    # MFMA results in VGPRs: the maxima read them with VALU, which cannot read
+    # AGPRs without a copy
+    "indexer.hip": NO_NAN + ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -81,41 +81,9 @@ __device__ __forceinline__ int vt_key(int cix, int j) {
   return 32 * (cix >> 2) + 16 * (j >> 2) + 4 * (cix & 3) + (j & 3);
 }
 
-// K staging chunk ch (0..1023, 16 bytes each): wave-instruction q = ch >> 6
-// covers bytes 64 (q & 1) .. + 63 of keys 16 (q >> 1) .. + 15, so that its
-// 16-lane write groups land on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int k_chunk_key(int ch) { return 16 * (ch >> 7) + (ch & 15); }
-__device__ __forceinline__ int k_chunk_part(int ch) { return 4 * ((ch >> 6) & 1) + ((ch >> 4) & 3); }
-
-// Two 16-byte reads 1 KB apart (the two halves of a 32-byte K operand).
-__device__ __forceinline__ v8i lds_read32x2(const uint8_t *p) {
-  const v4i lo = *reinterpret_cast<const v4i *>(p);
-  const v4i hi = *reinterpret_cast<const v4i *>(p + 1024);
-  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 __device__ __forceinline__ uint32_t bf16x2_from_e4m3(uint32_t packed, bool hi) {
   return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true)
                                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
-}
-
-// Max over the four lane groups (l, l ^ 16, l ^ 32, l ^ 48) holding one MFMA
-// column, with gfx950 row-swap permutes instead of LDS-routed shuffles.  The
-// swaps are written as asm (with the two wait states they need on either
-// side) so that the compiler cannot merge the two halves of a swap.
-__device__ __forceinline__ float group4_max_swap(float v) {
-  float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  v = fmaxf(a, b);
-  a = v;
-  b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
-}
-
-// Raw buffer resource over one 16 KB K or V tile (dword 3: 32-bit data format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const uint8_t *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, kPage * kD, 0x00020000);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
@@ -193,9 +161,7 @@ void attn_block_prefill_kernel(AttnArgs a, Grid gr) {
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
       const int ch = tid + j * kThreads;
-      const int key = k_chunk_key(ch), part = k_chunk_part(ch);
-      *reinterpret_cast<v4i *>(buf + 1024 * (2 * (key >> 4) + (part & 1)) + 16 * (16 * (part >> 1) + (key & 15))) =
-          kreg[j];
+      *reinterpret_cast<v4i *>(buf + k_tile_offset(k_chunk_key(ch), k_chunk_part(ch))) = kreg[j];
     }
     uint8_t *vt = buf + kKBytes;
 #pragma unroll

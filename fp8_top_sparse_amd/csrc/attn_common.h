@@ -35,15 +35,6 @@ struct Grid {
   float *part_ml;  // [splits, T, Hq, 4] = (m_ref, l, m_true, -)
 };
 
-// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads it
-// does not wait for outstanding global loads, so a tile prefetch issued before
-// it stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ v8i lds_read32(const uint8_t *p) {
   const v4i *q = reinterpret_cast<const v4i *>(p);
   v4i lo = q[0], hi = q[1];

@@ -92,4 +92,54 @@ __device__ __forceinline__ float group4_sum(float v) {
   return v;
 }
 
+// Max over the four lane groups (l, l ^ 16, l ^ 32, l ^ 48) holding one MFMA
+// column, with gfx950 row-swap permutes instead of LDS-routed shuffles.  The
+// swaps are written as asm (with the two wait states they need on either
+// side) so that the compiler cannot merge the two halves of a swap.
+__device__ __forceinline__ float group4_max_swap(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads it
+// does not wait for outstanding global loads, so a tile prefetch issued before
+// it stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Operand order for a 128-key x 128-byte e4m3 tile in LDS: the 16x16x128 A
+// operand (kt, hh) of lane l sits at 1024 * (2 * kt + hh) + 16 * l and holds
+// key 16 kt + (l & 15), bytes 32 (l >> 4) + 16 hh .. + 15, so every operand
+// fetch is one contiguous 1 KB wave read.  Staging chunk ch (0..1023, 16
+// bytes) maps to (key, part) so that wave-instruction q = ch >> 6 covers
+// bytes 64 (q & 1) .. + 63 of keys 16 (q >> 1) .. + 15: its 16-lane write
+// groups land on 16 distinct bank groups.
+__device__ __forceinline__ int k_chunk_key(int ch) { return 16 * (ch >> 7) + (ch & 15); }
+__device__ __forceinline__ int k_chunk_part(int ch) { return 4 * ((ch >> 6) & 1) + ((ch >> 4) & 3); }
+
+// Two 16-byte reads 1 KB apart (the two halves of a 32-byte K operand).
+__device__ __forceinline__ v8i lds_read32x2(const uint8_t *p) {
+  const v4i lo = *reinterpret_cast<const v4i *>(p);
+  const v4i hi = *reinterpret_cast<const v4i *>(p + 1024);
+  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ int k_tile_offset(int key, int part) {
+  return 1024 * (2 * (key >> 4) + (part & 1)) + 16 * (16 * (part >> 1) + (key & 15));
+}
+
+// Raw buffer resource over one 16 KB tile of 128 rows x 128 bytes (dword 3:
+// 32-bit data format); reads past the tile return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_tile_rsrc(const uint8_t *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, 128 * 128, 0x00020000);
+}
+
 }  // namespace fp8ts

@@ -5,22 +5,27 @@
 // per token) and sglang PR 30971 digest (implementation step 2, review
 // thread 2: ascending ids, -1 padding when the row has no more than k blocks).
 //
-// Two kernels:
-//  * score kernel (MFMA): a workgroup owns a tile of query tokens x all index
-//    heads (16-row MFMA column tiles) and a strided set of KV blocks.  Each
-//    wave streams its own block's 128 x 128 e4m3 keys straight from HBM into
-//    MFMA A-operand registers (S^T = K * Q^T, 16x16x128 e4m3 MFMA), reduces
-//    the causal maximum over the block's 128 keys per row and writes one fp32
-//    score per (head, token, block) to the workspace.  Tiles whose tokens all
-//    take the padding branch skip scoring entirely.
+// Kernels:
+//  * prefill score kernel (MFMA): a workgroup owns 256 rows = a tile of query
+//    tokens x all index heads and walks the blocks its last token can see.
+//    Each 16 KB idx_k page is staged once in LDS (double-buffered, MFMA
+//    operand order) and shared by all rows; S^T = K * Q^T on 16x16x128 e4m3
+//    MFMA, the causal maximum over the page's 128 keys stays in registers, and
+//    the fp32 scores are collected in LDS and written in contiguous per-row
+//    runs.  Tiles whose tokens all take the padding branch skip scoring.
+//  * decode score kernel: few rows per sequence, so each wave streams its own
+//    blocks' keys from HBM straight into MFMA operands and the blocks are
+//    split across workgroups.
 //  * select kernel (wave64): one wave per (head, token) row.  The k-th largest
-//    score is found by a 32-step bitwise search over order-preserving uint32
-//    keys (ballot + popcount per step); ties at the threshold go to the lower
-//    block id; the survivors are written by ordered compaction (ballot + mbcnt
-//    prefix), which yields ascending ids without a sort.  The earlier designs on
-//    the pages rank by pairwise comparison (an O(k^2) permutation, then a
-//    32-lane ballot rank); compaction in id order makes the ranking step
-//    unnecessary on 64-lane waves.
+//    score is found by an 8-bit radix select over order-preserving uint32 keys
+//    (four passes over a per-wave LDS histogram); ties at the threshold go to
+//    the lower block id; the survivors are written by ordered compaction
+//    (ballot + popcount prefix), which yields ascending ids without a sort.
+//    The designs on the pages rank by pairwise comparison (an O(k^2)
+//    permutation, then a 32-lane ballot rank); compaction in id order makes
+//    the ranking step unnecessary on 64-lane waves.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -29,12 +34,6 @@ namespace {
 
 constexpr int kPage = 128;
 constexpr int kD = 128;
-
-__device__ __forceinline__ v8i lds_read(const uint8_t *p) {
-  const v4i *q = reinterpret_cast<const v4i *>(p);
-  v4i lo = q[0], hi = q[1];
-  return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 
 struct SeqInfo {
   int b;       // sequence
@@ -168,13 +167,18 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
 
 // ------------------------------------------------------------ shared-tile score kernel
 // Prefill scoring: 4 waves x 4 column tiles = 256 rows (tokens x heads) share
-// each idx_k page, staged once in LDS; the next page is loaded into registers
-// while the current one is scored.
+// each idx_k page.  Pages are double-buffered in LDS in MFMA operand order
+// (contiguous 1 KB operand reads); page b + 1 is written from registers right
+// after the barrier of page b while page b + 2 is in flight (the barrier
+// orders LDS only).  Scores are collected in LDS for kFlush pages and written
+// as contiguous per-row runs instead of one 4-byte store per row and page.
 constexpr int kSWaves = 4, kSCols = 4, kSRows = kSWaves * kSCols * 16;
-constexpr int kKPitch = kD + 16;
+constexpr int kFlush = 16;
+constexpr int kScPitch = kFlush + 1;          // floats per row of the score buffer
 
 __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[kPage * kKPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kPage * kD];
+  __shared__ float sc_s[kSRows * kScPitch];
   constexpr int NT = kSWaves * 64;
   constexpr int K_PER = kPage * kD / 16 / NT;
   const int H = a.num_heads;
@@ -194,15 +198,13 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
   if (nb_tile <= a.topk) return;                 // every row takes the padding branch
 
   v8i qb[kSCols];
-  int row_p[kSCols], row_t[kSCols], row_h[kSCols];
+  int row_p[kSCols];
   int p_min = 0x7fffffff;
 #pragma unroll
   for (int c = 0; c < kSCols; ++c) {
     const int r = (wave * kSCols + c) * 16 + col;
     const int tt = t0 + r / H;
     const int h = r % H;
-    row_t[c] = cu0 + tt;
-    row_h[c] = h;
     row_p[c] = (tt < q_len) ? seq_len - q_len + tt : -1;
     if (row_p[c] >= 0) p_min = min(p_min, row_p[c]);
     v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -216,77 +218,115 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
   // smallest visible position over the wave's rows: blocks ending at or below it need no causal mask
   for (int off = 1; off < 64; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, 64));
 
-  // pages are prefetched two ahead into two register sets (the loop is
-  // unrolled by two so that each set is named statically)
-  v4i kst0[K_PER], kst1[K_PER];
-  bool valid0 = false, valid1 = false;
-  auto load = [&](int blk, v4i (&kst)[K_PER], bool &valid) __attribute__((always_inline)) {
-    if (blk >= nb_tile) return;
-    const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
-    valid = page >= 0 && page < a.num_pages;
-    const uint8_t *src = a.idx_k + (int64_t)(valid ? page : 0) * kPage * kD;
-#pragma unroll
-    for (int j = 0; j < K_PER; ++j)
-      kst[j] = valid ? *reinterpret_cast<const v4i *>(src + 16 * (tid + j * NT)) : (v4i){0, 0, 0, 0};
+  // page staging through registers: chunk ch of the page goes to its operand slot
+  v4i kreg[K_PER];
+  auto page_of = [&](int blk) -> int {
+    const int page = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
+    return (page >= 0 && page < a.num_pages) ? page : -1;
   };
-
-  const int64_t T = a.total_q;
-  auto step = [&](int blk, v4i (&kst)[K_PER], bool &valid) __attribute__((always_inline)) {
-    __syncthreads();
-    const bool cur_valid = valid;
+  auto load = [&](int page) {
+    if (page < 0) return;
+    const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.idx_k + (int64_t)page * kPage * kD);
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
       const int ch = tid + j * NT;
-      *reinterpret_cast<v4i *>(ks + (ch >> 3) * kKPitch + 16 * (ch & 7)) = kst[j];
+      kreg[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rk, k_chunk_key(ch) * kD + 16 * k_chunk_part(ch), 0, 0));
     }
-    __syncthreads();
-    load(blk + 2, kst, valid);                   // in flight during the next two pages
-
-    float mx[kSCols];
+  };
+  auto store = [&](int page, uint8_t *buf) {
+    if (page < 0) return;
 #pragma unroll
-    for (int c = 0; c < kSCols; ++c) mx[c] = -INFINITY;
-    if (cur_valid) {
-      const int key0 = blk * kPage;
-      const bool causal = key0 + kPage - 1 > p_min;   // wave-uniform
-      v8i ka[8];
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) ka[kt] = lds_read(ks + (kt * 16 + col) * kKPitch + 32 * g);
-#pragma unroll
-      for (int c = 0; c < kSCols; ++c) {
-        // eight independent MFMAs (distinct accumulators), then the row maximum
-        v4f acc[8];
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) acc[kt] = mfma_16x16x128_e4m3(ka[kt], qb[c], (v4f){0.f, 0.f, 0.f, 0.f});
-        float m = -INFINITY;
-        if (causal) {
-#pragma unroll
-          for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = key0 + kt * 16 + 4 * g + i > row_p[c] ? -INFINITY : acc[kt][i];
-              m = fmaxf(m, v);
-            }
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < 8; ++kt)
-            m = fmaxf(fmaxf(m, fmaxf(acc[kt][0], acc[kt][1])), fmaxf(acc[kt][2], acc[kt][3]));
-        }
-        mx[c] = m;
-      }
+    for (int j = 0; j < K_PER; ++j) {
+      const int ch = tid + j * NT;
+      *reinterpret_cast<v4i *>(buf + k_tile_offset(k_chunk_key(ch), k_chunk_part(ch))) = kreg[j];
     }
-#pragma unroll
-    for (int c = 0; c < kSCols; ++c) {
-      const float m = group4_max(mx[c]);
-      if (g == 0 && row_p[c] >= 0 && blk <= row_p[c] / kPage)
-        a.scores[((int64_t)row_h[c] * T + row_t[c]) * a.max_blocks + blk] = m * a.sigma;
+  };
+  // writes the collected scores of pages blk0 .. blk0 + n - 1: lanes run along a
+  // row's blocks, so each store instruction covers 4 rows x 64 contiguous bytes
+  const int64_t T = a.total_q;
+  auto flush = [&](int blk0, int n) {
+#pragma unroll 4
+    for (int e = tid; e < kSRows * kFlush; e += NT) {
+      const int r = e / kFlush, j = e % kFlush;
+      const int tt = t0 + r / H, h = r % H;
+      if (j >= n || tt >= q_len) continue;
+      const int blk = blk0 + j;
+      if (blk > (seq_len - q_len + tt) / kPage) continue;     // invisible block: never read
+      a.scores[((int64_t)h * T + cu0 + tt) * a.max_blocks + blk] = sc_s[r * kScPitch + j];
     }
   };
 
-  load(0, kst0, valid0);
-  load(1, kst1, valid1);
-  for (int blk = 0; blk < nb_tile; blk += 2) {
-    step(blk, kst0, valid0);
-    if (blk + 1 < nb_tile) step(blk + 1, kst1, valid1);
+  int cur_page = page_of(0), next_page = nb_tile > 1 ? page_of(1) : -1;
+  load(cur_page);
+  store(cur_page, kbuf[0]);
+  load(next_page);
+  // drain the prologue loads once: otherwise the wait-count analysis makes
+  // the first MFMA of every page wait for the in-flight prefetch
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  for (int blk = 0; blk < nb_tile; ++blk) {
+    lds_barrier();             // page blk is in LDS; every wave is done with page blk - 1
+    const uint8_t *ks = kbuf[blk & 1];
+    const bool valid = cur_page >= 0;
+    if (blk + 1 < nb_tile) {
+      store(next_page, kbuf[(blk + 1) & 1]);
+      cur_page = next_page;
+      next_page = blk + 2 < nb_tile ? page_of(blk + 2) : -1;
+      load(next_page);         // in flight during this page and the next
+    }
+    float mx[kSCols];
+#pragma unroll
+    for (int c = 0; c < kSCols; ++c) mx[c] = -INFINITY;
+    if (valid) {
+      const int key0 = blk * kPage;
+      const bool causal = key0 + kPage - 1 > p_min;   // wave-uniform
+      // two 16-key sub-tiles at a time, a running maximum per column tile:
+      // keeps the MFMA results few enough to stay in VGPRs.  The causal test
+      // is wave-uniform, so each variant of the page loop is straight-line code.
+      auto page_max = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+          const v8i k0 = lds_read32x2(ks + 2048 * (2 * kp) + 16 * lane);
+          const v8i k1 = lds_read32x2(ks + 2048 * (2 * kp + 1) + 16 * lane);
+          v4f s0[kSCols], s1[kSCols];
+#pragma unroll
+          for (int c = 0; c < kSCols; ++c) {
+            s0[c] = mfma_16x16x128_e4m3(k0, qb[c], (v4f){0.f, 0.f, 0.f, 0.f});
+            s1[c] = mfma_16x16x128_e4m3(k1, qb[c], (v4f){0.f, 0.f, 0.f, 0.f});
+          }
+#pragma unroll
+          for (int c = 0; c < kSCols; ++c) {
+            if constexpr (decltype(masked)::value) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kq = key0 + 32 * kp + 4 * g + i;
+                mx[c] = fmaxf(mx[c], kq > row_p[c] ? -INFINITY : s0[c][i]);
+                mx[c] = fmaxf(mx[c], kq + 16 > row_p[c] ? -INFINITY : s1[c][i]);
+              }
+            } else {
+              mx[c] = fmaxf(fmaxf(mx[c], fmaxf(s0[c][0], s0[c][1])), fmaxf(s0[c][2], s0[c][3]));
+              mx[c] = fmaxf(fmaxf(mx[c], fmaxf(s1[c][0], s1[c][1])), fmaxf(s1[c][2], s1[c][3]));
+            }
+          }
+        }
+      };
+      if (causal) {
+        page_max(std::true_type{});
+      } else {
+        page_max(std::false_type{});
+      }
+    }
+    const int slot = blk % kFlush;
+#pragma unroll
+    for (int c = 0; c < kSCols; ++c) {
+      const float m = group4_max_swap(mx[c]);
+      if (g == 0) sc_s[((wave * kSCols + c) * 16 + col) * kScPitch + slot] = m * a.sigma;
+    }
+    if (slot == kFlush - 1 || blk == nb_tile - 1) {
+      lds_barrier();           // every wave's scores of this group are in LDS
+      flush(blk - slot, slot + 1);
+    }
   }
 }
 
