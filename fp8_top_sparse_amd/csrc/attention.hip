@@ -472,9 +472,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
 }
 
 // ---------------------------------------------------------------- host side
+#ifndef FP8TS_DECODE_CHUNK
+#define FP8TS_DECODE_CHUNK 32
+#endif
+constexpr int kDecodeChunk = FP8TS_DECODE_CHUNK;   // union blocks per decode workgroup
+
 struct Plan {
   int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads,
-              // 4 block prefill, double-buffered
+              // 4 block prefill, pipelined, 5 block decode, pipelined
   Grid gr;
   int64_t nblocks;
   size_t lds;
@@ -519,6 +524,24 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
     }
     pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
     pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
+    // decode: the pipelined decode kernel (small single-buffered tiles, several
+    // workgroups per CU) streams ~kDecodeChunk blocks of the union per workgroup
+    if (kDecodeChunk > 0 && pl.kind == 1) {
+      Grid dg = gr;
+      dg.TT = block_decode_rows() / gr.G > 0 ? block_decode_rows() / gr.G : 1;
+      dg.n_tiles = (max_q_len + dg.TT - 1) / dg.TT;
+      dg.NL = dg.TT * dg.n_il;
+      int ubound = dg.n_il * (dg.TT < max_q_len ? dg.TT : max_q_len) * topk;
+      if (ubound > max_blocks) ubound = max_blocks;
+      dg.splits = (ubound + kDecodeChunk - 1) / kDecodeChunk;
+      if (dg.splits < 1) dg.splits = 1;
+      if (block_decode_rows() >= gr.G && block_decode_lds(dg) <= kMaxLds) {
+        gr = dg;
+        pl.kind = 5;
+        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+        pl.lds = block_decode_lds(gr);
+      }
+    }
     // prefill tiles go to the pipelined kernel when its LDS fits; otherwise to
     // the single-buffered one, whose tiles are 256 rows
     if (pl.kind == 0) {
@@ -594,6 +617,7 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
                           kPrefillWaves * 64, a, stream); break;
     case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
     case 4: st = launch_block_prefill(a, pl.gr, pl.nblocks, stream); break;
+    case 5: st = launch_block_decode(a, pl.gr, pl.nblocks, stream); break;
     case 2: st = launch_k(attn_kernel<576, 512, 8, 1, 64, false>, pl, 512, a, stream); break;
     default: st = launch_k(attn_kernel<576, 512, 1, 1, 64, false>, pl, 64, a, stream); break;
   }

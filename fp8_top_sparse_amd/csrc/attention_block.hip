@@ -45,9 +45,10 @@ namespace {
 #ifndef FP8TS_PREFILL_BUFS
 #define FP8TS_PREFILL_BUFS 2
 #endif
+#ifndef FP8TS_PREFILL_WAVES
+#define FP8TS_PREFILL_WAVES 16
+#endif
 constexpr int kD = 128;
-constexpr int kRows = FP8TS_PREFILL_ROWS;  // query rows per workgroup
-constexpr int kBufs = FP8TS_PREFILL_BUFS;  // K/V tile buffers in LDS (2: one barrier per tile)
 constexpr int kNdt = kD / 16;             // 16-dim output tiles
 // K and V^T tiles are stored in MFMA operand order: every operand fetch is
 // one contiguous 1 KB wave read (64 lanes x 16 bytes), which the LDS serves
@@ -59,19 +60,35 @@ constexpr int kNdt = kD / 16;             // 16-dim output tiles
 constexpr int kKBytes = kPage * kD;
 constexpr int kVBytes = kD * kPage * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
-constexpr int kMetaOff = kBufs * kBufBytes;
 constexpr int kKChunks = kPage * kD / 16;           // 16-byte chunks of a K tile
 constexpr int kVUnits = (kD / 4) * 16 * 2;          // 4-dim x 4-key units of a V tile
 
 #ifndef FP8TS_PREFILL_WAVES
 #define FP8TS_PREFILL_WAVES 16
 #endif
-constexpr int kWaves = FP8TS_PREFILL_WAVES;         // 16: 16 rows per wave, 8: 32 rows per wave
-constexpr int kThreads = kWaves * 64;
-constexpr int kCols = kRows / 16 / kWaves;          // 16-row column tiles per wave
-static_assert(kCols * 16 * kWaves == kRows && kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "tile");
-// single-buffered workgroups are sized so that two share a CU
-constexpr int kWavesPerSimd = (kBufs == 1 ? 2 : 1) * kWaves / 4;
+// Kernel configuration: WAVES waves split ROWS query rows into 16-row column
+// tiles; BUFS K/V tile buffers in LDS (2: one barrier per tile; 1: two
+// barriers per tile, and the workgroup is sized so that two share a CU).
+template <int WAVES, int ROWS, int BUFS>
+struct Cfg {
+  static constexpr int kWaves = WAVES;
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int kRows = ROWS;
+  static constexpr int kBufs = BUFS;
+  static constexpr int kCols = ROWS / 16 / WAVES;
+  static constexpr int kMetaOff = BUFS * kBufBytes;
+  static constexpr int kWavesPerSimd = (BUFS == 1 ? 2 : 1) * WAVES / 4;
+  static_assert(kCols * 16 * WAVES == ROWS, "tile");
+  static_assert(kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "staging");
+};
+// prefill: 256-row tiles, 16 waves, double-buffered
+using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BUFS>;
+// decode: few rows per kv head, so small single-buffered workgroups that
+// share a CU keep more pages in flight
+#ifndef FP8TS_DECODE_WAVES
+#define FP8TS_DECODE_WAVES 4
+#endif
+using DecodeCfg = Cfg<FP8TS_DECODE_WAVES, FP8TS_DECODE_WAVES * 16, 1>;
 
 // Tile-relative key held in slot j (0..7) of 16-byte V^T chunk cix (0..15):
 // chunk cix = 4 * m + g serves the PV MFMA of 32-key group m for lane group g,
@@ -86,8 +103,10 @@ __device__ __forceinline__ uint32_t bf16x2_from_e4m3(uint32_t packed, bool hi) {
                                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
-void attn_block_prefill_kernel(AttnArgs a, Grid gr) {
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWavesPerSimd)))
+void attn_block_kernel(AttnArgs a, Grid gr) {
+  constexpr int kThreads = C::kThreads, kCols = C::kCols, kBufs = C::kBufs, kMetaOff = C::kMetaOff;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -383,21 +402,33 @@ void attn_block_prefill_kernel(AttnArgs a, Grid gr) {
   attn_epilogue<kCols, kNdt>(a, gr, split, g, br.row_ok, br.row_t, br.row_h, o, m_ref, m_true, lsum);
 }
 
-}  // namespace
-
-size_t block_prefill_lds(const Grid &gr) {
-  return (size_t)kMetaOff + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + 2 * (size_t)gr.W * 32);
+template <class C>
+size_t block_lds(const Grid &gr) {
+  return (size_t)C::kMetaOff + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + 2 * (size_t)gr.W * 32);
 }
 
-int block_prefill_rows() { return kWaves * kCols * 16; }
-
-int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
-  const size_t lds = block_prefill_lds(gr);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_block_prefill_kernel),
+template <class C>
+int launch_block(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream, const char *what) {
+  const size_t lds = block_lds<C>(gr);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_block_kernel<C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return fail(FP8TS_EHIP, "sparse_attn_fwd: LDS attribute: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(attn_block_prefill_kernel, dim3((unsigned)nblocks), dim3(kThreads), lds, stream, a, gr);
-  return check_launch("sparse_attn_fwd (block prefill)");
+  hipLaunchKernelGGL(attn_block_kernel<C>, dim3((unsigned)nblocks), dim3(C::kThreads), lds, stream, a, gr);
+  return check_launch(what);
+}
+
+}  // namespace
+
+size_t block_prefill_lds(const Grid &gr) { return block_lds<PrefillCfg>(gr); }
+int block_prefill_rows() { return PrefillCfg::kRows; }
+int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
+  return launch_block<PrefillCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
+}
+
+size_t block_decode_lds(const Grid &gr) { return block_lds<DecodeCfg>(gr); }
+int block_decode_rows() { return DecodeCfg::kRows; }
+int launch_block_decode(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
+  return launch_block<DecodeCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block decode)");
 }
 
 }  // namespace fp8ts

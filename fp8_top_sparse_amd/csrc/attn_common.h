@@ -218,10 +218,14 @@ __device__ __forceinline__ void attn_epilogue(const AttnArgs &a, const Grid &gr,
   }
 }
 
-// Block-mode prefill kernel with double-buffered K/V tiles (attention_block.hip).
+// Block-mode kernels with pipelined K/V tiles (attention_block.hip): prefill
+// (256-row tiles, double-buffered) and decode (small single-buffered tiles).
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 size_t block_prefill_lds(const Grid &gr);
 int block_prefill_rows();
 int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
+size_t block_decode_lds(const Grid &gr);
+int block_decode_rows();
+int launch_block_decode(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 
 }  // namespace fp8ts
