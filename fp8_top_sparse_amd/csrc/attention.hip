@@ -479,7 +479,8 @@ constexpr int kDecodeChunk = FP8TS_DECODE_CHUNK;   // union blocks per decode wo
 
 struct Plan {
   int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads,
-              // 4 block prefill, pipelined, 5 block decode, pipelined
+              // 4 block prefill, pipelined, 5 block decode, pipelined,
+              // 6 token 128 heads, pipelined
   Grid gr;
   int64_t nblocks;
   size_t lds;
@@ -557,7 +558,24 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
       }
     }
   } else {
-    if (hq % 128 == 0) {
+    if (hq % token_mla_rows() == 0) {
+      // 128 heads per workgroup; few tokens split their lists so that the
+      // grid still covers the GPU (at least 256 keys per split)
+      gr.n_tiles = hq / token_mla_rows();
+      const int64_t wgs = (int64_t)total_q * gr.n_tiles;
+      gr.splits = 1;
+      if (wgs < 256) {
+        const int want = (int)((256 + wgs - 1) / wgs);
+        const int most = topk / 256 > 1 ? topk / 256 : 1;
+        gr.splits = want < most ? want : most;
+      }
+      pl.kind = 6;
+      pl.lds = token_mla_lds(topk, gr.splits);
+      if (pl.lds > kMaxLds) {
+        pl.kind = 2;
+        pl.lds = lds_base<576, 512, 64>();
+      }
+    } else if (hq % 128 == 0) {
       pl.kind = 2;
       gr.n_tiles = hq / 128;
       gr.splits = 1;
@@ -618,6 +636,13 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
     case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
     case 4: st = launch_block_prefill(a, pl.gr, pl.nblocks, stream); break;
     case 5: st = launch_block_decode(a, pl.gr, pl.nblocks, stream); break;
+    case 6:
+      if (token_mla_fits(a)) {
+        st = launch_token_mla(a, pl.gr, pl.nblocks, stream);
+        break;
+      }
+      pl.lds = lds_base<576, 512, 64>();   // caches past 2 GB: the unpipelined kernel
+      [[fallthrough]];
     case 2: st = launch_k(attn_kernel<576, 512, 8, 1, 64, false>, pl, 512, a, stream); break;
     default: st = launch_k(attn_kernel<576, 512, 1, 1, 64, false>, pl, 64, a, stream); break;
   }

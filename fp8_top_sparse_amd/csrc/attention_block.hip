@@ -90,19 +90,6 @@ using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BU
 #endif
 using DecodeCfg = Cfg<FP8TS_DECODE_WAVES, FP8TS_DECODE_WAVES * 16, 1>;
 
-// Tile-relative key held in slot j (0..7) of 16-byte V^T chunk cix (0..15):
-// chunk cix = 4 * m + g serves the PV MFMA of 32-key group m for lane group g,
-// whose slots j < 4 are keys 4g + j of the even 16-key S^T tile and slots
-// j >= 4 keys 4g + j - 4 of the odd one.
-__device__ __forceinline__ int vt_key(int cix, int j) {
-  return 32 * (cix >> 2) + 16 * (j >> 2) + 4 * (cix & 3) + (j & 3);
-}
-
-__device__ __forceinline__ uint32_t bf16x2_from_e4m3(uint32_t packed, bool hi) {
-  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
-}
-
 template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWavesPerSimd)))
 void attn_block_kernel(AttnArgs a, Grid gr) {

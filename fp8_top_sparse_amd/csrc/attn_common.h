@@ -47,6 +47,19 @@ __device__ __forceinline__ v8i gload32(const uint8_t *p) {
   return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Tile-relative key held in slot j (0..7) of 16-byte V^T chunk cix (0..15):
+// chunk cix = 4 * m + g serves the PV MFMA of 32-key group m for lane group g,
+// whose slots j < 4 are keys 4g + j of the even 16-key S^T tile and slots
+// j >= 4 keys 4g + j - 4 of the odd one.
+__device__ __forceinline__ int vt_key(int cix, int j) {
+  return 32 * (cix >> 2) + 16 * (j >> 2) + 4 * (cix & 3) + (j & 3);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_from_e4m3(uint32_t packed, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
+}
+
 // V^T tile layout (bf16): row d holds the keys of dimension d.  Keys are
 // grouped in 8-byte units of 4; the unit index is XOR-swizzled with the row's
 // 16-dim group (d / 16), and the row pitch is 8 bytes past a multiple of 256,
@@ -227,5 +240,12 @@ int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hip
 size_t block_decode_lds(const Grid &gr);
 int block_decode_rows();
 int launch_block_decode(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
+// Token-mode MLA kernel with pipelined K/V tiles (attention_token.hip): 128 q
+// heads of one token per workgroup.  token_mla_fits: the caches are small
+// enough for its 32-bit byte offsets.
+size_t token_mla_lds(int topk, int splits);
+int token_mla_rows();
+bool token_mla_fits(const AttnArgs &a);
+int launch_token_mla(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 
 }  // namespace fp8ts
