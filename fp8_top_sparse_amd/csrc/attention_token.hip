@@ -56,8 +56,12 @@ constexpr int kVtOff = 2 * kKBytes;
 constexpr int kIdxOff = kVtOff + 2 * kVtBytes;   // the split's index list (int32)
 constexpr int kVUnits = (kKT / 4) * (kDv / 4);   // 4-key x 4-dim units of a V tile
 constexpr int V_PER = kVUnits / kThreads;
-// Byte offset of an absent key: past the end of any cache the kernel accepts,
-// so the buffer load returns zeros.
+// K rows reach LDS through a structured buffer resource (record = one cache
+// row): the hardware forms base + index * stride + offset and writes zeros
+// for an index at or past the record count, so an absent key (stored as -1,
+// i.e. index 0xFFFFFFFF) needs no address arithmetic.  V rows are gathered
+// with byte offsets (indexed dword gathers measured slower); an absent key
+// gets an offset past the end of the cache, which also reads zeros.
 constexpr uint32_t kNoRow = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -140,25 +144,26 @@ void attn_token_kernel(AttnArgs a, Grid gr) {
   // and, when w & 3 == 0, the tail of key tile kt: its lanes all read key
   // 16 (w >> 2) + (l & 15).  V: the units of a thread cover dims 4 d4 .. + 3
   // of keys 16 jh + 4 cix + i.
-  const uint32_t ks = (uint32_t)a.k_row_stride & 0xFFFFFFu, vs = (uint32_t)a.v_row_stride & 0xFFFFFFu;
+  const uint32_t vs = (uint32_t)a.v_row_stride & 0xFFFFFFu;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int k_kt = wave_s >> 2, k_kc = wave_s & 3;
   const bool k_tail = k_kc == 0;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(a.k), (short)0, (int)((a.num_kv - 1) * a.k_row_stride + kDqk), 0x00020000);
+      const_cast<uint8_t *>(a.k), (short)a.k_row_stride, (int)a.num_kv, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(a.v), (short)0, (int)((a.num_kv - 1) * a.v_row_stride + kDv), 0x00020000);
   const int jh = tid & 1, d4 = (tid >> 1) & 127;
   uint32_t vreg[V_PER][4];
   auto dma_k = [&](int it, uint8_t *kb) {
-    const uint32_t ko = row_offset(idx_s[it * kKT + 16 * k_kt + col], ks);
+    const int id = idx_s[it * kKT + 16 * k_kt + col];
     uint8_t *slot = kb + 1024 * (2 * wave_s);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)slot, 16, ko + 128 * k_kc + 32 * g, 0, 0, 0);
-    // (the instruction offset would move the LDS destination as well)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(slot + 1024), 16, ko + 128 * k_kc + 32 * g + 16, 0, 0, 0);
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(rk, (lds_void *)slot, 16, id, 128 * k_kc + 32 * g, 0, 0, 0);
+    // (an instruction offset would move the LDS destination as well)
+    __builtin_amdgcn_struct_ptr_buffer_load_lds(rk, (lds_void *)(slot + 1024), 16, id, 128 * k_kc + 32 * g + 16, 0, 0,
+                                                0);
     if (k_tail)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kb + kKMain + 1024 * k_kt), 16, ko + 512 + 16 * g, 0,
-                                               0, 0);
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(rk, (lds_void *)(kb + kKMain + 1024 * k_kt), 16, id, 512 + 16 * g, 0,
+                                                  0, 0);
   };
   auto load_v = [&](int it) {
     const int32_t *ids = idx_s + it * kKT;
@@ -327,10 +332,10 @@ void attn_token_kernel(AttnArgs a, Grid gr) {
 #pragma unroll
         for (int c = 0; c < kCols; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[c], o[dt][c]);
       }
-      // V^T operand reads run four MFMAs ahead
-      sched_reads(4);
-      sched_mfma_then_reads<kNdt - 4, 1>();
-      sched_mfma_then_reads<4, 0>();
+      // V^T operand reads run six MFMAs ahead
+      sched_reads(6);
+      sched_mfma_then_reads<kNdt - 6, 1>();
+      sched_mfma_then_reads<6, 0>();
       // the K DMA of tile it + 1 lands before the next barrier (the V loads
       // of tile it + 2 are waited for right after it anyway)
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -366,13 +371,12 @@ size_t token_mla_lds(int topk, int splits) {
 int token_mla_rows() { return kRowsPerWg; }
 
 bool token_mla_fits(const AttnArgs &a) {
-  // byte offsets into the caches stay below kNoRow; ids and strides fit the
-  // 24-bit multiply
+  // the K row stride fits the buffer resource's 14-bit stride field; V byte
+  // offsets stay below kNoRow and its ids and stride fit the 24-bit multiply
   const int64_t lim = (int64_t)kNoRow - 4096;
-  return a.dqk == kDqk && a.dv == kDv && a.num_kv > 0 && a.num_kv < (1 << 24) &&
-         a.k_row_stride >= kDqk && a.k_row_stride < (1 << 24) && a.v_row_stride >= kDv &&
-         a.v_row_stride < (1 << 24) && a.k_row_stride % 16 == 0 && a.v_row_stride % 4 == 0 &&
-         (a.num_kv - 1) * a.k_row_stride + kDqk < lim && (a.num_kv - 1) * a.v_row_stride + kDv < lim;
+  return a.dqk == kDqk && a.dv == kDv && a.num_kv > 0 && a.num_kv < (1 << 24) && a.k_row_stride >= kDqk &&
+         a.k_row_stride < 16384 && a.k_row_stride % 16 == 0 && a.v_row_stride >= kDv &&
+         a.v_row_stride < (1 << 24) && a.v_row_stride % 4 == 0 && (a.num_kv - 1) * a.v_row_stride + kDv < lim;
 }
 
 int launch_token_mla(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
