@@ -34,11 +34,18 @@
 //    128-row workgroups share a CU): tile t+1 is written from registers while
 //    tile t is computed and tile t+2 is in flight from HBM.  Barriers order
 //    LDS only, so the prefetch stays in flight across them.
+//  * Prefill waves own 32 rows (two column tiles), so every operand read from
+//    LDS feeds two MFMAs, and scheduling-group barriers place the operand
+//    reads ahead of their MFMAs (two waves per SIMD leave room in registers
+//    for reads in flight).
 #include "attn_common.h"
 
 namespace fp8ts {
 namespace {
 
+#ifndef FP8TS_PV_AHEAD
+#define FP8TS_PV_AHEAD 2
+#endif
 #ifndef FP8TS_PREFILL_ROWS
 #define FP8TS_PREFILL_ROWS 256
 #endif
@@ -46,7 +53,7 @@ namespace {
 #define FP8TS_PREFILL_BUFS 2
 #endif
 #ifndef FP8TS_PREFILL_WAVES
-#define FP8TS_PREFILL_WAVES 16
+#define FP8TS_PREFILL_WAVES 8
 #endif
 constexpr int kD = 128;
 constexpr int kNdt = kD / 16;             // 16-dim output tiles
@@ -63,9 +70,6 @@ constexpr int kBufBytes = kKBytes + kVBytes;
 constexpr int kKChunks = kPage * kD / 16;           // 16-byte chunks of a K tile
 constexpr int kVUnits = (kD / 4) * 16 * 2;          // 4-dim x 4-key units of a V tile
 
-#ifndef FP8TS_PREFILL_WAVES
-#define FP8TS_PREFILL_WAVES 16
-#endif
 // Kernel configuration: WAVES waves split ROWS query rows into 16-row column
 // tiles; BUFS K/V tile buffers in LDS (2: one barrier per tile; 1: two
 // barriers per tile, and the workgroup is sized so that two share a CU).
@@ -81,7 +85,8 @@ struct Cfg {
   static_assert(kCols * 16 * WAVES == ROWS, "tile");
   static_assert(kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "staging");
 };
-// prefill: 256-row tiles, 16 waves, double-buffered
+// prefill: 256-row tiles, 8 waves of 32 rows (each K or V^T operand read
+// feeds two MFMAs), double-buffered
 using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BUFS>;
 // decode: few rows per kv head, so small single-buffered workgroups that
 // share a CU keep more pages in flight
@@ -89,6 +94,17 @@ using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BU
 #define FP8TS_DECODE_WAVES 4
 #endif
 using DecodeCfg = Cfg<FP8TS_DECODE_WAVES, FP8TS_DECODE_WAVES * 16, 1>;
+
+// Instruction-order constraints for the scheduler (LDS reads ahead of the
+// MFMAs that consume them): N LDS reads, then R x (M MFMAs, N LDS reads).
+template <int R, int M, int N>
+__device__ __forceinline__ void sched_mfma_then_reads() {
+  if constexpr (R > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(0x100, N, 0);
+    sched_mfma_then_reads<R - 1, M, N>();
+  }
+}
 
 template <class C>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWavesPerSimd)))
@@ -275,6 +291,10 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
 #pragma unroll
             for (int c = 0; c < kCols; ++c) s[kt][c] = mfma_16x16x128_e4m3(ka, qb[c], cinit[c]);
           }
+          // K operand reads (two LDS reads each) run two operands ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          sched_mfma_then_reads<2, kCols, 2>();
+          sched_mfma_then_reads<2, kCols, 0>();
           // ---- causal mask, only where some row of the wave needs one
           const int kpos0 = key_base + 64 * h;
           bool part = false;
@@ -357,6 +377,10 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
               for (int c = 0; c < kCols; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[m][c], o[dt][c]);
             }
           }
+          // V^T operand reads run FP8TS_PV_AHEAD MFMA pairs ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, FP8TS_PV_AHEAD, 0);
+          sched_mfma_then_reads<2 * kNdt - FP8TS_PV_AHEAD, kCols, 1>();
+          sched_mfma_then_reads<FP8TS_PV_AHEAD, kCols, 0>();
         }
       }
       if (it + 1 < n_iter) {
