@@ -485,6 +485,7 @@ struct Plan {
   int64_t nblocks;
   size_t lds;
   size_t ws;
+  size_t vt_bytes;   // block prefill: pre-converted V^T tiles in the workspace (0: converted in the kernel)
 };
 
 template <int DQK, int DV, int KT>
@@ -549,6 +550,10 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
       if (block_prefill_lds(gr) <= kMaxLds) {
         pl.kind = 4;
         pl.lds = block_prefill_lds(gr);
+        // sequences spanning several tiles visit each page many times over:
+        // convert every V page to its V^T tile once, up front
+        const size_t vt = (size_t)batch * max_blocks * hkv * vt_page_bytes();
+        if (gr.n_tiles >= 4 && vt <= ((size_t)1 << 30)) pl.vt_bytes = vt;
       } else if (gr.TT != 256 / gr.G) {
         gr.TT = 256 / gr.G > 0 ? 256 / gr.G : 1;
         gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
@@ -594,6 +599,7 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
   if (gr.splits > 1) {
     pl.ws = (size_t)gr.splits * total_q * hq * dv * 4 + (size_t)gr.splits * total_q * hq * 16 + 256;
   }
+  pl.ws += pl.vt_bytes;   // V^T tiles after the partials (256-byte aligned)
   return pl;
 }
 
@@ -628,6 +634,7 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
     pl.gr.part_o = reinterpret_cast<float *>(ws);
     pl.gr.part_ml = reinterpret_cast<float *>(ws + (size_t)pl.gr.splits * a.total_q * a.hq * a.dv * 4);
   }
+  if (pl.vt_bytes) pl.gr.vt_pages = static_cast<uint8_t *>(a.workspace) + (pl.ws - pl.vt_bytes);
   if (pl.nblocks == 0) return FP8TS_OK;
   int st = FP8TS_OK;
   switch (pl.kind) {

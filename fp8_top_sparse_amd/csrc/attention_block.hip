@@ -73,8 +73,11 @@ constexpr int kVUnits = (kD / 4) * 16 * 2;          // 4-dim x 4-key units of a 
 // Kernel configuration: WAVES waves split ROWS query rows into 16-row column
 // tiles; BUFS K/V tile buffers in LDS (2: one barrier per tile; 1: two
 // barriers per tile, and the workgroup is sized so that two share a CU).
-template <int WAVES, int ROWS, int BUFS>
+// PRE: V^T tiles come pre-converted from the workspace (vt_pages_kernel), and
+// both K and V^T are staged by buffer-to-LDS DMA, with no staging registers.
+template <int WAVES, int ROWS, int BUFS, bool PRE = false>
 struct Cfg {
+  static constexpr bool kPre = PRE;
   static constexpr int kWaves = WAVES;
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kRows = ROWS;
@@ -88,12 +91,72 @@ struct Cfg {
 // prefill: 256-row tiles, 8 waves of 32 rows (each K or V^T operand read
 // feeds two MFMAs), double-buffered
 using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BUFS>;
+using PrefillPreCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, 2, true>;
 // decode: few rows per kv head, so small single-buffered workgroups that
 // share a CU keep more pages in flight
 #ifndef FP8TS_DECODE_WAVES
 #define FP8TS_DECODE_WAVES 4
 #endif
 using DecodeCfg = Cfg<FP8TS_DECODE_WAVES, FP8TS_DECODE_WAVES * 16, 1>;
+
+// V staging unit u (0..1023) of a 128-key x 128-dim tile: 4 dims x 4 keys,
+// half jh = u & 1 of V^T chunk cix = u >> 6, dims 4 d4 .. + 3 with
+// d4 = (u >> 1) & 31.  Its raw dword i (e4m3 dims 4 d4 .. + 3 of one key) is
+// at vt_unit_src(u, i) in the page.
+__device__ __forceinline__ int vt_unit_src(int u, int i) {
+  return vt_key(u >> 6, 4 * (u & 1) + i) * kD + 4 * ((u >> 1) & 31);
+}
+
+// Writes unit u (raw dwords w) widened to bf16 into the V^T tile vt.
+__device__ __forceinline__ void vt_store_unit(uint8_t *vt, int u, const uint32_t (&v)[4]) {
+  const int jh = u & 1, d4 = (u >> 1) & 31, cix = u >> 6;
+  // rotate so that byte s of w[i] is dim 4 * d4 + ((s + rot) & 3): the 16
+  // lanes sharing a write cycle then hit 16 distinct bank groups
+  const int rot = (d4 >> 2) & 3;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbyte(v[i], v[i], rot);
+  // 4x4 byte transpose: x[s] = byte s of keys 0..3
+  const uint32_t t0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  const uint32_t x[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                         __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int d = 4 * d4 + ((s4 + rot) & 3);
+    const v2i pr = {(int)bf16x2_from_e4m3(x[s4], false), (int)bf16x2_from_e4m3(x[s4], true)};
+    *reinterpret_cast<v2i *>(vt + 1024 * (4 * (d >> 4) + (cix >> 2)) + 16 * (16 * (cix & 3) + (d & 15)) + 8 * jh) = pr;
+  }
+}
+
+// V^T of the page behind every (block-table slot, kv head), in the prefill
+// kernel's LDS operand order (bf16, 32 KB each), so that the prefill tiles,
+// which each visit a page many times over, stage it by DMA alone.  Slot
+// (b * max_blocks + j) * hkv + kvh; slots without a valid page are skipped.
+__global__ __launch_bounds__(256) void vt_pages_kernel(AttnArgs a, uint8_t *vt_pages) {
+  __shared__ __attribute__((aligned(16))) uint8_t vt_s[kVBytes];
+  const int slot = blockIdx.x;
+  const int kvh = slot % a.hkv;
+  const int page = a.block_table[slot / a.hkv];
+  if (page < 0 || page >= a.num_kv) return;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rv = make_tile_rsrc(a.v + ((int64_t)page * a.hkv + kvh) * kPage * kD);
+#pragma unroll
+  for (int j = 0; j < kVUnits / 256; ++j) {
+    const int u = tid + 256 * j;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vt_unit_src(u, i), 0, 0);
+    vt_store_unit(vt_s, u, w);
+  }
+  __syncthreads();
+  v4i *dst = reinterpret_cast<v4i *>(vt_pages + (int64_t)slot * kVBytes);
+  for (int i = tid; i < kVBytes / 16; i += 256) dst[i] = reinterpret_cast<const v4i *>(vt_s)[i];
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Instruction-order constraints for the scheduler (LDS reads ahead of the
 // MFMAs that consume them): N LDS reads, then R x (M MFMAs, N LDS reads).
@@ -154,8 +217,8 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   constexpr int V_PER = kVUnits / kThreads;
   const int64_t kv_head_stride = (int64_t)kPage * kD;
   const int kvh_s = __builtin_amdgcn_readfirstlane(br.kvh);
-  v4i kreg[K_PER];
-  uint32_t vreg[V_PER][4];
+  v4i kreg[C::kPre ? 1 : K_PER];
+  uint32_t vreg[C::kPre ? 1 : V_PER][4];
   // page ids are workgroup-uniform: each tile is read through buffer
   // resources (scalar base, 16 KB extent) with 32-bit lane offsets, so no
   // 64-bit per-lane address stays live across the loop
@@ -171,11 +234,9 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           rk, k_chunk_key(tid + j * kThreads) * kD + 16 * k_chunk_part(tid + j * kThreads), 0, 0));
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) {
-      const int u = tid + j * kThreads;
-      const int jh = u & 1, d4 = (u >> 1) & 31, cix = u >> 6;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        vreg[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vt_key(cix, 4 * jh + i) * kD + 4 * d4, 0, 0);
+        vreg[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vt_unit_src(tid + j * kThreads, i), 0, 0);
     }
   };
   auto store_tile = [&](int page, uint8_t *buf) {
@@ -185,30 +246,34 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       const int ch = tid + j * kThreads;
       *reinterpret_cast<v4i *>(buf + k_tile_offset(k_chunk_key(ch), k_chunk_part(ch))) = kreg[j];
     }
-    uint8_t *vt = buf + kKBytes;
 #pragma unroll
-    for (int j = 0; j < V_PER; ++j) {
-      const int u = tid + j * kThreads;
-      const int jh = u & 1, d4 = (u >> 1) & 31, cix = u >> 6;
-      // rotate so that byte s of w[i] is dim 4 * d4 + ((s + rot) & 3): the
-      // 16 lanes sharing a write cycle then hit 16 distinct bank groups
-      const int rot = (d4 >> 2) & 3;
-      uint32_t w[4];
+    for (int j = 0; j < V_PER; ++j) vt_store_unit(buf + kKBytes, tid + j * kThreads, vreg[j]);
+  };
+  // PRE: tile it by DMA.  K operand slot s (kt = s >> 1, hh = s & 1) of lane
+  // l holds key 16 kt + (l & 15), bytes 32 (l >> 4) + 16 hh; the V^T tile is
+  // copied as it stands in the workspace.  16 + 32 wave-sized 1 KB slots.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](int it_, uint8_t *buf) {
+    const int page = __builtin_amdgcn_readfirstlane(plist[it_]);
+    if (page < 0) return;
+    const int blk = __builtin_amdgcn_readfirstlane(ulist[lo + it_]);
+    const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.k + ((int64_t)page * a.hkv + kvh_s) * kv_head_stride);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        gr.vt_pages + (((int64_t)br.b * a.max_blocks + blk) * a.hkv + kvh_s) * kVBytes, (short)0, kVBytes,
+        0x00020000);
+    constexpr int kW = kThreads / 64;
+    static_assert(16 % kW == 0, "K slots per wave");
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbyte(vreg[j][i], vreg[j][i], rot);
-      // 4x4 byte transpose: x[s] = byte s of keys 0..3
-      const uint32_t t0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
-      const uint32_t t1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
-      const uint32_t t2 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
-      const uint32_t t3 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
-      const uint32_t x[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
-                             __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+    for (int j = 0; j < 16 / kW; ++j) {
+      const int s = wave_s + kW * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(buf + 1024 * s), 16,
+                                               (16 * (s >> 1) + col) * kD + 32 * g + 16 * (s & 1), 0, 0, 0);
+    }
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int d = 4 * d4 + ((s4 + rot) & 3);
-        const v2i pr = {(int)bf16x2_from_e4m3(x[s4], false), (int)bf16x2_from_e4m3(x[s4], true)};
-        *reinterpret_cast<v2i *>(vt + 1024 * (4 * (d >> 4) + (cix >> 2)) + 16 * (16 * (cix & 3) + (d & 15)) + 8 * jh) = pr;
-      }
+    for (int j = 0; j < 32 / kW; ++j) {
+      const int s = wave_s + kW * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(buf + kKBytes + 1024 * s), 16, 1024 * s + 16 * lane,
+                                               0, 0, 0);
     }
   };
 
@@ -244,11 +309,15 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   for (int pass = 0; pass < 2; ++pass) {
     bool overflow = false;
     if (n_iter > 0) {
-      load_tile(plist[0]);
-      store_tile(plist[0], smem);
+      if constexpr (C::kPre) {
+        dma_tile(0, smem);
+      } else {
+        load_tile(plist[0]);
+        store_tile(plist[0], smem);
+      }
       fetch_meta(0);
     }
-    if (n_iter > 1) load_tile(plist[1]);
+    if (!C::kPre && n_iter > 1) load_tile(plist[1]);
     // drain the prologue loads here, once: otherwise the wait-count analysis
     // makes the first MFMA of every tile wait for the in-flight prefetch
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -270,8 +339,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       // tile it - 1 used, and start loading tile it + 2: this VALU and LDS
       // work overlaps the previous tile's PV products still in the MFMA pipe
       if (kBufs == 2 && it + 1 < n_iter) {
-        store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
-        if (it + 2 < n_iter) load_tile(plist[it + 2]);
+        if constexpr (C::kPre) {
+          dma_tile(it + 1, smem + ((it + 1) & 1) * kBufBytes);
+        } else {
+          store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
+          if (it + 2 < n_iter) load_tile(plist[it + 2]);
+        }
       }
       if (__any(any_sel)) {
         const int key_base = blk * kPage;
@@ -377,10 +450,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
               for (int c = 0; c < kCols; ++c) o[dt][c] = mfma_16x16x32_bf16(va, pb[m][c], o[dt][c]);
             }
           }
-          // V^T operand reads run FP8TS_PV_AHEAD MFMA pairs ahead
-          __builtin_amdgcn_sched_group_barrier(0x100, FP8TS_PV_AHEAD, 0);
-          sched_mfma_then_reads<2 * kNdt - FP8TS_PV_AHEAD, kCols, 1>();
-          sched_mfma_then_reads<FP8TS_PV_AHEAD, kCols, 0>();
+          // V^T operand reads run kPvAhead MFMA groups ahead (the DMA-staged
+          // configuration has the registers for more reads in flight)
+          constexpr int kPvAhead = C::kPre ? 4 : FP8TS_PV_AHEAD;
+          __builtin_amdgcn_sched_group_barrier(0x100, kPvAhead, 0);
+          sched_mfma_then_reads<2 * kNdt - kPvAhead, kCols, 1>();
+          sched_mfma_then_reads<kPvAhead, kCols, 0>();
         }
       }
       if (it + 1 < n_iter) {
@@ -391,6 +466,8 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           if (it + 2 < n_iter) load_tile(plist[it + 2]);
         }
       }
+      // PRE: the DMA of tile it + 1 lands before the next barrier
+      if constexpr (C::kPre) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
     // rare second pass: restart from the exact row maxima seen in the first one
     if (pass == 1 || !__syncthreads_or(overflow)) break;
@@ -432,8 +509,13 @@ int launch_block(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t
 
 size_t block_prefill_lds(const Grid &gr) { return block_lds<PrefillCfg>(gr); }
 int block_prefill_rows() { return PrefillCfg::kRows; }
+size_t vt_page_bytes() { return kVBytes; }
 int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream) {
-  return launch_block<PrefillCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
+  if (!gr.vt_pages) return launch_block<PrefillCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
+  const int64_t slots = (int64_t)a.batch * a.max_blocks * a.hkv;
+  hipLaunchKernelGGL(vt_pages_kernel, dim3((unsigned)slots), dim3(256), 0, stream, a, gr.vt_pages);
+  if (int st = check_launch("sparse_attn_fwd (V^T pages)")) return st;
+  return launch_block<PrefillPreCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
 }
 
 size_t block_decode_lds(const Grid &gr) { return block_lds<DecodeCfg>(gr); }

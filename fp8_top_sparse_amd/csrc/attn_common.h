@@ -33,6 +33,7 @@ struct Grid {
   int W;           // block: 32-bit words per block bitmap
   float *part_o;   // [splits, T, Hq, DV]
   float *part_ml;  // [splits, T, Hq, 4] = (m_ref, l, m_true, -)
+  uint8_t *vt_pages;  // block prefill: [batch * max_blocks * hkv] V^T tiles (bf16, LDS operand order), or null
 };
 
 __device__ __forceinline__ v8i lds_read32(const uint8_t *p) {
@@ -236,6 +237,7 @@ __device__ __forceinline__ void attn_epilogue(const AttnArgs &a, const Grid &gr,
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 size_t block_prefill_lds(const Grid &gr);
 int block_prefill_rows();
+size_t vt_page_bytes();   // one pre-converted V^T tile
 int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 size_t block_decode_lds(const Grid &gr);
 int block_decode_rows();

@@ -178,7 +178,11 @@ int indexer_topk(const uint8_t *idx_q, const uint8_t *idx_k, int64_t num_pages,
  * out             device bf16 [total_q, num_q_heads, head_dim_v].
  * max_logits, lse device float [total_q, num_q_heads].
  * workspace       device scratch of sparse_attn_workspace_size(...) bytes
- *                 (may be 0 bytes / NULL when that size is 0).
+ *                 (may be 0 bytes / NULL when that size is 0): partial
+ *                 results of split key lists (decode, small token-mode
+ *                 workloads) and, for block-mode prefill over sequences of
+ *                 several query tiles, one bf16 V^T tile (32 KB) per
+ *                 block-table slot and KV head, converted once per call.
  * Errors: FP8TS_EINVAL for malformed arguments; FP8TS_EUNSUPPORTED for head
  * dims, page sizes or head counts outside the ranges above (a token-mode
  * head_dim_v other than 512 in particular, as the pages' MLA kernel rejects).

@@ -165,8 +165,12 @@ def test_attention_block_mode_validation(lib):
 
 
 def test_attention_workspace_sizes(lib):
-    # prefill block mode and large-head token mode need no workspace
-    assert lib.sparse_attn_workspace_size(1, 1, 8192, 8192, 16, 2, 4, 128, 64, 64) == 0
+    # block prefill over sequences of several tiles keeps one bf16 V^T tile
+    # (128 keys x 128 dims) per (block-table slot, kv head)
+    assert lib.sparse_attn_workspace_size(1, 1, 8192, 8192, 16, 2, 4, 128, 64, 64) == 64 * 2 * 128 * 128 * 2
+    assert lib.sparse_attn_workspace_size(1, 3, 3 * 4096, 4096, 16, 2, 4, 128, 64, 40) == 3 * 40 * 2 * 128 * 128 * 2
+    # short prefill (fewer than 4 tiles per sequence) and large-head token mode need none
+    assert lib.sparse_attn_workspace_size(1, 1, 96, 96, 16, 2, 4, 128, 64, 64) == 0
     assert lib.sparse_attn_workspace_size(0, 0, 4096, 0, 128, 1, 1, 512, 2048, 0) == 0
     # decode splits the block union: partial O plus (m, l) per split
     n = lib.sparse_attn_workspace_size(1, 64, 64, 1, 16, 2, 4, 128, 64, 256)
