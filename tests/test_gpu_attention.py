@@ -269,6 +269,15 @@ def test_block_varlen_prefix_decode_mix_with_sink(gpu):
     assert_attention_close(got, ref, "varlen")
 
 
+def test_block_short_prefill_converts_in_kernel(gpu):
+    """Fewer than 4 query tiles per sequence: V is converted inside the tile
+    loop instead of by the V^T pre-pass (the long cases above use the pre-pass)."""
+    c = block_case([3000, 2100], [80, 70], seed=17, topk=8, sink=True)
+    got = run_block(gpu, c, q_scale=1.1, v_scale=0.7)
+    ref = ref_block(c, q_scale=1.1, v_scale=0.7)
+    assert_attention_close(got, ref, "short prefill")
+
+
 def test_block_decode_batch(gpu):
     rng = np.random.default_rng(12)
     seq = [int(x) for x in rng.integers(1, 12000, 14)] + [1, 128, 129]
