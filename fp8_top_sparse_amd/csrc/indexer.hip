@@ -16,6 +16,8 @@
 //  * decode score kernel: few rows per sequence, so each wave streams its own
 //    blocks' keys from HBM straight into MFMA operands and the blocks are
 //    split across workgroups.
+//  * when no row can see more than k blocks (max_blocks <= k), a fill kernel
+//    writes the closed form 0 .. nb - 1, -1 ... and nothing is scored.
 //  * select kernel (wave64): one wave per (head, token) row.  The k-th largest
 //    score is found by an 8-bit radix select over order-preserving uint32 keys
 //    (four passes over a per-wave LDS histogram); ties at the threshold go to
@@ -434,6 +436,21 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
   }
 }
 
+// Every row has at most k visible blocks (max_blocks <= k): the ids are the
+// closed form 0 .. nb - 1, then -1, whatever the scores.  One wave per
+// (head, token) row, as in the select kernel, writing the row contiguously.
+__global__ __launch_bounds__(256) void indexer_fill_kernel(IndexerArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t T = a.total_q;
+  if (row >= (int64_t)a.num_heads * T) return;
+  const int t = (int)(row % T);
+  const SeqInfo si = find_seq(a.cu_seqlens_q, a.seq_lens, a.batch, t);
+  const int nb = min(si.p < 0 ? 0 : si.p / kPage + 1, a.max_blocks);
+  int32_t *out = a.out_ids + row * a.topk;
+  for (int j = lane; j < a.topk; j += 64) out[j] = j < nb ? j : -1;
+}
+
 }  // namespace
 
 size_t indexer_workspace_bytes(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
@@ -446,6 +463,12 @@ int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
   // 16-row tile when few tokens per sequence (decode), whose waves stream
   // their own pages with the blocks split across workgroups.
   const int H = a.num_heads;
+  if (a.max_blocks <= a.topk) {
+    // no row can have more than k blocks: nothing to score or rank
+    const int64_t rows = (int64_t)H * a.total_q;
+    hipLaunchKernelGGL(indexer_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    return check_launch("indexer_topk (closed form)");
+  }
   const bool small = (int64_t)a.max_q_len * H <= 16;
   if (small) {
     const int TT = 16 / H;

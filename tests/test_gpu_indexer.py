@@ -87,6 +87,17 @@ def test_varlen_prefix_and_decode_mix(gpu):
     assert_ids_equal(got, ref, "varlen")
 
 
+@pytest.mark.parametrize("topk", [40, 41])
+def test_varlen_closed_form_when_no_row_exceeds_k(gpu, topk):
+    """max_blocks <= k: every row is the closed form 0 .. nb-1, -1 ... (varlen
+    with a prefix, plain prefill and decode rows)."""
+    iq, ik, bt, cu, sl, mq = make_case([5000, 1300, 128, 4097], [700, 1300, 1, 1], seed=40, H=4)
+    assert bt.shape[1] <= topk
+    got = run(gpu, iq, ik, bt, cu, sl, mq, topk)
+    ref = OI.indexer_topk(iq, ik, bt, cu, sl, sm_scale=0.088, topk=topk)
+    assert_ids_equal(got, ref, f"closed form k={topk}")
+
+
 @pytest.mark.parametrize("H", [1, 2, 8, 16])
 def test_head_counts(gpu, H):
     iq, ik, bt, cu, sl, mq = make_case([1500, 700], [300, 700], seed=H, H=H)
