@@ -253,10 +253,8 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   // l holds key 16 kt + (l & 15), bytes 32 (l >> 4) + 16 hh; the V^T tile is
   // copied as it stands in the workspace.  16 + 32 wave-sized 1 KB slots.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  auto dma_tile = [&](int it_, uint8_t *buf) {
-    const int page = __builtin_amdgcn_readfirstlane(plist[it_]);
+  auto dma_tile = [&](int page, int blk, uint8_t *buf) {
     if (page < 0) return;
-    const int blk = __builtin_amdgcn_readfirstlane(ulist[lo + it_]);
     const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.k + ((int64_t)page * a.hkv + kvh_s) * kv_head_stride);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         gr.vt_pages + (((int64_t)br.b * a.max_blocks + blk) * a.hkv + kvh_s) * kVBytes, (short)0, kVBytes,
@@ -306,11 +304,22 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       t_sel[c] = has_page && br.row_ok[c] && ((bits[br.row_li[c] * gr.W + (t_blk >> 5)] >> (t_blk & 31)) & 1u);
   };
 
+  // PRE: the page and block of tile it + 1 are loaded from LDS during tile
+  // it - 1 (m_page_v, m_blk_v: consumed a tile later, so their latency never
+  // shows), and the selection words of tile it + 1 during tile it (m_word).
+  int m_page_v = 0, m_blk_v = 0;
+  uint32_t m_word[kCols];
   for (int pass = 0; pass < 2; ++pass) {
     bool overflow = false;
+    if constexpr (C::kPre) {
+      if (n_iter > 1) {
+        m_page_v = plist[1];
+        m_blk_v = ulist[lo + 1];
+      }
+    }
     if (n_iter > 0) {
       if constexpr (C::kPre) {
-        dma_tile(0, smem);
+        dma_tile(__builtin_amdgcn_readfirstlane(plist[0]), __builtin_amdgcn_readfirstlane(ulist[lo]), smem);
       } else {
         load_tile(plist[0]);
         store_tile(plist[0], smem);
@@ -338,13 +347,23 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       // stage tile it + 1 (loaded during the previous tile) into the buffer
       // tile it - 1 used, and start loading tile it + 2: this VALU and LDS
       // work overlaps the previous tile's PV products still in the MFMA pipe
-      if (kBufs == 2 && it + 1 < n_iter) {
-        if constexpr (C::kPre) {
-          dma_tile(it + 1, smem + ((it + 1) & 1) * kBufBytes);
-        } else {
-          store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
-          if (it + 2 < n_iter) load_tile(plist[it + 2]);
+      int n_page = -1, n_blk = 0;   // PRE: tile it + 1
+      if constexpr (C::kPre) {
+        if (it + 1 < n_iter) {
+          n_page = __builtin_amdgcn_readfirstlane(m_page_v);
+          n_blk = __builtin_amdgcn_readfirstlane(m_blk_v);
+          dma_tile(n_page, n_blk, smem + ((it + 1) & 1) * kBufBytes);
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) m_word[c] = bits[br.row_li[c] * gr.W + (n_blk >> 5)];
+          if (it + 2 < n_iter) {
+            m_page_v = plist[it + 2];
+            m_blk_v = ulist[lo + it + 2];
+          }
         }
+      }
+      if (!C::kPre && kBufs == 2 && it + 1 < n_iter) {
+        store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
+        if (it + 2 < n_iter) load_tile(plist[it + 2]);
       }
       if (__any(any_sel)) {
         const int key_base = blk * kPage;
@@ -459,7 +478,14 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
         }
       }
       if (it + 1 < n_iter) {
-        fetch_meta(it + 1);
+        if constexpr (C::kPre) {
+          t_blk = n_blk;
+#pragma unroll
+          for (int c = 0; c < kCols; ++c)
+            t_sel[c] = n_page >= 0 && br.row_ok[c] && ((m_word[c] >> (n_blk & 31)) & 1u);
+        } else {
+          fetch_meta(it + 1);
+        }
         if (kBufs == 1) {
           lds_barrier();     // every wave is done with tile it
           store_tile(plist[it + 1], smem);
