@@ -17,12 +17,13 @@ e4m3       OCP e4m3fn decode / round-to-nearest-even encode with saturation.
 quantize   per-tensor fp8 quantization ("stored value = x / scale").
 indexer    lightning-indexer block scores and ascending top-k block ids.
 attention  sparse attention forward (token mode and block mode).
+cache_store  quantize new K / V / index-K rows into a paged fp8 cache.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against closed
 forms, exhaustive enumeration, brute force and library routines; the pin for
 each function is listed in its docstring.
 """
 
-from . import e4m3, quantize, indexer, attention  # noqa: F401
+from . import e4m3, quantize, indexer, attention, cache_store  # noqa: F401
 
-__all__ = ["e4m3", "quantize", "indexer", "attention"]
+__all__ = ["e4m3", "quantize", "indexer", "attention", "cache_store"]
