@@ -94,6 +94,71 @@ def block_attention_flops(ids: np.ndarray, pos: np.ndarray, hq: int, hidx: int, 
     return keys * (hq // hidx) * 2 * (d_qk + d_v)
 
 
+def token_positions(cu_seqlens_q, seq_lens):
+    """(sequence id, absolute position) of every flattened query token."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    seq = np.repeat(np.arange(len(sl)), np.diff(cu))
+    start = cu[:-1][seq]
+    return seq, sl[seq] - (cu[1:] - cu[:-1])[seq] + (np.arange(int(cu[-1])) - start)
+
+
+def measure_cache_store(fts, wl, block: bool, reps: int) -> dict:
+    """fp8_cache_store of the workload's new keys into fresh caches, HBM-bound.
+
+    Block workloads store K and V ([T, Hkv, 128] bf16 each, with the
+    workload's scales) and index-K ([T, 128]) into paged caches through the
+    block table; token workloads pack latent (512) + rope (64) rows into the
+    flat [S, 576] array.  Algorithmic bytes: 2 read + 1 written per element,
+    plus 8 per slot per call.  A 512 MiB buffer is read between repetitions
+    (outside the events) so the inputs come from HBM, not the 256 MB
+    last-level cache; reading leaves no dirty lines whose write-back would be
+    charged to the store.
+    """
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(77)
+    if block:
+        T = wl.q_bf16.shape[0]
+        P, Hkv = wl.k_cache8.shape[0], wl.k_cache8.shape[1]
+        seq, pos = token_positions(wl.cu_seqlens_q, wl.seq_lens)     # this step's new keys
+        slots = torch.from_numpy(wl.block_table[seq, pos // PAGE].astype(np.int64) * PAGE + pos % PAGE).cuda()
+        jobs = []
+        for heads, scale in ((Hkv, wl.k_scale), (Hkv, wl.v_scale), (1, wl.idx_k_scale)):
+            x = torch.randn((T, heads, 128), generator=g, device="cuda").to(torch.bfloat16)
+            cache = torch.empty((P, heads, PAGE, 128), dtype=torch.uint8, device="cuda")
+            jobs.append((x, None, cache, scale))
+        n_tok = T
+    else:
+        S = wl.kv8.shape[0]
+        slots = torch.arange(S, dtype=torch.int64, device="cuda")
+        kv_a = torch.randn((S, 512), generator=g, device="cuda").to(torch.bfloat16)
+        k_pe = torch.randn((S, 64), generator=g, device="cuda").to(torch.bfloat16)
+        jobs = [(kv_a, k_pe, torch.empty((S, 576), dtype=torch.uint8, device="cuda"), wl.k_scale)]
+        n_tok = S
+    elems = sum(x.numel() + (0 if x2 is None else x2.numel()) for x, x2, _, _ in jobs)
+    nbytes = 3 * elems + 8 * n_tok * len(jobs)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+
+    def run():
+        for x, x2, cache, scale in jobs:
+            fts.fp8_cache_store(x, slots, cache, scale=scale, x2=x2)
+
+    run()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.mean(times))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "launches": len(jobs), "bytes": int(nbytes), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -192,8 +257,7 @@ def main():
 
     # algorithmic work, counted from the path's own selections
     if block:
-        from oracle.indexer import positions   # host-side position arithmetic for the work count
-        _, pos = positions(wl.cu_seqlens_q, wl.seq_lens)
+        _, pos = token_positions(wl.cu_seqlens_q, wl.seq_lens)
         ids_h = ids.cpu().numpy()
         flops = block_attention_flops(ids_h, pos, Hq, Hidx, D, D)
         quant_bytes = 3 * (wl.q_bf16.size + wl.idx_q_bf16.size)
@@ -272,6 +336,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": committed_traffic(args.workload)},
     }
+
+    result["cache_store"] = measure_cache_store(fts, wl, block, args.steps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, block)

@@ -9,6 +9,7 @@ Functions (same names as the C ABI in ``include/fp8ts.h``):
 * :func:`fp8_quantize`     bf16/fp16 tensor -> e4m3 bytes (per-tensor scale).
 * :func:`indexer_topk`     lightning-indexer ascending top-k block ids.
 * :func:`sparse_attn_fwd`  sparse attention forward (token or block mode).
+* :func:`fp8_cache_store`  quantize new K / V / index-K rows into a paged e4m3 cache.
 
 fp8 tensors are exchanged as ``torch.uint8`` holding e4m3fn bytes
 (``torch.float8_e4m3fn`` inputs are accepted and viewed as bytes).
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "indexer_topk_workspace_size": ([_i32, _i32, _i32], _sz),
     "indexer_topk": ([_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                       _fp, _fp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "fp8_cache_store": ([_vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _i32,
+                         _fp, _vp], ctypes.c_int),
     "sparse_attn_workspace_size": ([_i32] * 10, _sz),
     "sparse_attn_fwd": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp, _vp,
@@ -277,5 +280,62 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
     return out, max_logits, lse
 
 
-__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "load", "flatten_to_2d", "EXPORTED",
+def _token_head_view(x: torch.Tensor, name: str):
+    """(N, H, D, token_stride, head_stride) of a [N, D] or [N, H, D] source."""
+    if x.dim() == 2:
+        x = x.unsqueeze(1)
+    if x.dim() != 3:
+        raise ValueError(f"{name} must be [N, D] or [N, H, D]")
+    if x.shape[-1] > 1 and x.stride(-1) != 1:
+        raise ValueError(f"{name}: last dim must be contiguous")
+    n, h, d = x.shape
+    return n, h, d, x.stride(0), x.stride(1)
+
+
+def fp8_cache_store(x: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Tensor, *,
+                    scale: Optional[float] = None, x2: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Quantize ``x`` (and ``x2``) and write token n into slot ``slot_mapping[n]`` of ``cache``.
+
+    x ``[N, H, D]`` or ``[N, D]`` bf16/fp16 (any token / head strides);
+    slot_mapping int64 ``[N]`` (negative = skip); cache e4m3 bytes
+    ``[pages, H, page_size, D + D2]``, ``[pages, page_size, D + D2]`` (one head)
+    or ``[S, D + D2]`` (flat rows, page_size 1).  Returns ``cache`` (written in place).
+    """
+    lib = load()
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float16:
+        dt = FP16
+    else:
+        raise ValueError(f"x must be bf16 or fp16, got {x.dtype}")
+    n, h, d, xts, xhs = _token_head_view(x, "x")
+    d2, x2ts, x2hs = 0, 0, 0
+    if x2 is not None:
+        if x2.dtype != x.dtype:
+            raise ValueError("x2 must have the dtype of x")
+        n2, h2, d2, x2ts, x2hs = _token_head_view(x2, "x2")
+        if (n2, h2) != (n, h):
+            raise ValueError("x2 must have the token and head counts of x")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must be a contiguous int64 tensor with one slot per token")
+    cb = _bytes(cache)
+    if not cb.is_contiguous():
+        raise ValueError("cache must be contiguous")
+    if cb.dim() == 4:
+        pages, ch, page, row = cb.shape
+    elif cb.dim() == 3:
+        (pages, page, row), ch = cb.shape, 1
+    elif cb.dim() == 2:
+        (pages, row), ch, page = cb.shape, 1, 1
+    else:
+        raise ValueError("cache must be [pages, H, page, row], [pages, page, row] or [S, row]")
+    if ch != h or row != d + d2:
+        raise ValueError(f"cache heads/row ({ch}, {row}) do not match the sources ({h}, {d} + {d2})")
+    _check(lib.fp8_cache_store(_ptr(x), _ptr(x2), dt, n, h, d, d2, xts, xhs, x2ts, x2hs, _ptr(slot_mapping),
+                               _ptr(cb), pages, page, _scale(scale), _stream(stream)))
+    return cache
+
+
+__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "load", "flatten_to_2d", "EXPORTED",
            "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

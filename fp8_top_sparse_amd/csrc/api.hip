@@ -72,6 +72,68 @@ int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int
   return launch_quantize(x, x_dtype, rows, cols, x_row_stride, out, out_row_stride, has, inv, stream);
 }
 
+int fp8_cache_store(const void *x, const void *x2, int32_t x_dtype, int64_t num_tokens,
+                    int32_t num_heads, int32_t dim, int32_t dim2, int64_t x_token_stride,
+                    int64_t x_head_stride, int64_t x2_token_stride, int64_t x2_head_stride,
+                    const int64_t *slot_mapping, uint8_t *cache, int64_t num_pages,
+                    int32_t page_size, const float *scale, hipStream_t stream) {
+  const char *fn = "fp8_cache_store";
+  if (x_dtype != FP8TS_BF16 && x_dtype != FP8TS_FP16)
+    return fail(FP8TS_EINVAL, "%s: x_dtype must be 0 (bf16) or 1 (fp16), got %d", fn, x_dtype);
+  if (num_tokens < 0 || num_pages < 0) return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  if (num_heads < 1 || dim < 1 || dim2 < 0 || page_size < 1)
+    return fail(FP8TS_EINVAL, "%s: need num_heads >= 1, dim >= 1, dim2 >= 0, page_size >= 1 (got %d, %d, %d, %d)",
+                fn, num_heads, dim, dim2, page_size);
+  if ((dim2 > 0) != (x2 != nullptr)) return fail(FP8TS_EINVAL, "%s: x2 must be given exactly when dim2 > 0", fn);
+  bool has = false;
+  float sv = 1.0f;
+  if (int st = read_scale(fn, "scale", scale, &has, &sv)) return st;
+  if (num_tokens == 0) return FP8TS_OK;
+  if (!x || !slot_mapping || !cache) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (num_pages == 0) return fail(FP8TS_EINVAL, "%s: empty cache", fn);
+  // every (token, head) row of a source must be a separate run of elements
+  auto rows_ok = [&](int64_t ts, int64_t hs, int32_t d) {
+    if (ts < 0 || hs < 0) return false;
+    if (num_heads > 1 && hs < d) return false;
+    return num_tokens == 1 || ts >= (int64_t)(num_heads - 1) * hs + d;
+  };
+  if (!rows_ok(x_token_stride, x_head_stride, dim))
+    return fail(FP8TS_EINVAL, "%s: x strides (%lld, %lld) overlap rows of %d elements", fn,
+                (long long)x_token_stride, (long long)x_head_stride, dim);
+  if (dim2 > 0 && !rows_ok(x2_token_stride, x2_head_stride, dim2))
+    return fail(FP8TS_EINVAL, "%s: x2 strides (%lld, %lld) overlap rows of %d elements", fn,
+                (long long)x2_token_stride, (long long)x2_head_stride, dim2);
+  const int64_t row = (int64_t)dim + dim2;
+  // the kernel indexes chunks and slots in 32 bits
+  if (num_tokens * num_heads * row >= ((int64_t)1 << 31) || num_pages * page_size >= ((int64_t)1 << 31))
+    return fail(FP8TS_EUNSUPPORTED, "%s: more than 2^31 - 1 elements or slots in one call", fn);
+  const size_t cb = (size_t)(num_pages * num_heads * page_size * row);
+  const size_t xb = (size_t)((num_tokens - 1) * x_token_stride + (int64_t)(num_heads - 1) * x_head_stride + dim) * 2;
+  if (overlaps(x, xb, cache, cb)) return fail(FP8TS_EINVAL, "%s: cache overlaps x", fn);
+  if (dim2 > 0) {
+    const size_t x2b = (size_t)((num_tokens - 1) * x2_token_stride + (int64_t)(num_heads - 1) * x2_head_stride + dim2) * 2;
+    if (overlaps(x2, x2b, cache, cb)) return fail(FP8TS_EINVAL, "%s: cache overlaps x2", fn);
+  }
+  if (overlaps(slot_mapping, (size_t)num_tokens * 8, cache, cb)) return fail(FP8TS_EINVAL, "%s: cache overlaps slot_mapping", fn);
+  StoreArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.x2 = static_cast<const uint16_t *>(x2);
+  a.x_ts = x_token_stride;
+  a.x_hs = x_head_stride;
+  a.x2_ts = x2_token_stride;
+  a.x2_hs = x2_head_stride;
+  a.slots = slot_mapping;
+  a.cache = cache;
+  a.num_tokens = num_tokens;
+  a.num_slots = num_pages * page_size;
+  a.heads = num_heads;
+  a.dim = dim;
+  a.dim2 = dim2;
+  a.page_size = page_size;
+  const float inv = has ? 1.0f / sv : 1.0f;   // fp32 reciprocal, rounded once
+  return launch_cache_store(a, x_dtype, has, inv, stream);
+}
+
 size_t indexer_topk_workspace_size(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
   if (total_q <= 0 || num_heads <= 0 || max_blocks <= 0) return 0;
   return indexer_workspace_bytes(total_q, num_heads, max_blocks);

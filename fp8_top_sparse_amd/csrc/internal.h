@@ -20,6 +20,18 @@ int launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_
                     uint8_t *out, int64_t out_stride, bool has_scale, float scale_inv,
                     hipStream_t stream);
 
+// ---- paged cache store
+struct StoreArgs {
+  const uint16_t *x, *x2;        // [N, heads, dim] / [N, heads, dim2] (x2 may be null when dim2 == 0)
+  int64_t x_ts, x_hs, x2_ts, x2_hs;  // token / head strides in elements
+  const int64_t *slots;          // [N]
+  uint8_t *cache;                // [num_slots / page_size, heads, page_size, dim + dim2]
+  int64_t num_tokens, num_slots;
+  int32_t heads, dim, dim2, page_size;
+};
+int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scale_inv,
+                       hipStream_t stream);
+
 // ---- indexer
 struct IndexerArgs {
   const uint8_t *idx_q;

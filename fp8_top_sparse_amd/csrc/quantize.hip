@@ -154,7 +154,101 @@ int launch_typed(const uint16_t *x, int64_t rows, int64_t cols, int64_t xs, uint
   return check_launch("fp8_quantize");
 }
 
+// ---- paged cache store: quantize token rows and scatter them by slot.
+//
+// Token n, head h, element c of x (and c of x2, placed after x in the row)
+// goes to cache[page][h][off][c] with page = slot / page_size and
+// off = slot % page_size; slots < 0 or >= num_slots write nothing.  The
+// pool stores value / scale like the queries (sglang PR 30971 digest,
+// implementation step 4); the two-source row is the MLA latent + rope pack
+// (sglang PR 25460 digest, implementation step 2).
+//
+// HBM-bound: 2 + 1 bytes per element plus one 8-byte slot per token.  One
+// thread per 8-element chunk of a (token, head) row; a row's chunks are
+// adjacent threads, so each cache row is written as one contiguous run.
+// Index arithmetic is 32-bit (the host keeps chunk and slot counts below
+// 2^31); only byte offsets into the cache are formed in 64 bits.  Each thread
+// issues the loads of two chunks before converting either.
+template <bool VEC>
+__device__ __forceinline__ bool locate(const StoreArgs &a, uint32_t g, uint32_t cpr, uint32_t c1,
+                                       const uint16_t *&src, uint8_t *&dst) {
+  constexpr uint32_t per = VEC ? 8 : 1;
+  const uint32_t r = g / cpr;
+  const uint32_t c = g - r * cpr;
+  const uint32_t n = r / (uint32_t)a.heads;
+  const uint32_t h = r - n * (uint32_t)a.heads;
+  const int64_t slot = a.slots[n];
+  if (slot < 0 || slot >= a.num_slots) return false;
+  const uint32_t page = (uint32_t)slot / (uint32_t)a.page_size;
+  const uint32_t off = (uint32_t)slot - page * (uint32_t)a.page_size;
+  const int64_t row = a.dim + a.dim2;
+  dst = a.cache + (((int64_t)page * a.heads + h) * a.page_size + off) * row;
+  if (c < c1) {
+    src = a.x + (int64_t)n * a.x_ts + (int64_t)h * a.x_hs + c * per;
+    dst += c * per;
+  } else {
+    src = a.x2 + (int64_t)n * a.x2_ts + (int64_t)h * a.x2_hs + (c - c1) * per;
+    dst += a.dim + (c - c1) * per;
+  }
+  return true;
+}
+
+template <int DT, bool HAS_SCALE, bool VEC>
+__global__ __launch_bounds__(256) void cache_store_kernel(StoreArgs a, float s) {
+  constexpr uint32_t per = VEC ? 8 : 1;
+  const uint32_t c1 = (uint32_t)a.dim / per;
+  const uint32_t cpr = c1 + (uint32_t)a.dim2 / per;
+  const uint32_t total = (uint32_t)a.num_tokens * (uint32_t)a.heads * cpr;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += 2 * stride) {
+    const uint16_t *s0 = nullptr, *s1 = nullptr;
+    uint8_t *d0 = nullptr, *d1 = nullptr;
+    const bool k0 = locate<VEC>(a, g, cpr, c1, s0, d0);
+    const bool k1 = g + stride < total && locate<VEC>(a, g + stride, cpr, c1, s1, d1);
+    if constexpr (VEC) {
+      v4u w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
+      if (k0) w0 = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(s0));
+      if (k1) w1 = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(s1));
+      if (k0) *reinterpret_cast<v2u *>(d0) = quant8<DT, HAS_SCALE>(w0, s);
+      if (k1) *reinterpret_cast<v2u *>(d1) = quant8<DT, HAS_SCALE>(w1, s);
+    } else {
+      if (k0) *d0 = quant1<DT, HAS_SCALE>(*s0, s);
+      if (k1) *d1 = quant1<DT, HAS_SCALE>(*s1, s);
+    }
+  }
+}
+
+template <int DT, bool HAS_SCALE>
+int launch_store_typed(const StoreArgs &a, float s, hipStream_t stream) {
+  const bool vec = a.dim % 8 == 0 && a.dim2 % 8 == 0 && a.x_ts % 8 == 0 && a.x_hs % 8 == 0 &&
+                   (uintptr_t)a.x % 16 == 0 && (uintptr_t)a.cache % 8 == 0 &&
+                   (a.dim2 == 0 || (a.x2_ts % 8 == 0 && a.x2_hs % 8 == 0 && (uintptr_t)a.x2 % 16 == 0));
+  const int64_t per = vec ? 8 : 1;
+  const int64_t total = a.num_tokens * a.heads * ((a.dim + a.dim2) / per);
+  int64_t blocks = (total + 511) / 512;      // two chunks per thread
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (vec) {
+    hipLaunchKernelGGL((cache_store_kernel<DT, HAS_SCALE, true>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, s);
+  } else {
+    hipLaunchKernelGGL((cache_store_kernel<DT, HAS_SCALE, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, s);
+  }
+  return check_launch("fp8_cache_store");
+}
+
 }  // namespace
+
+int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scale_inv,
+                       hipStream_t stream) {
+  if (dtype == FP8TS_BF16) {
+    return has_scale ? launch_store_typed<FP8TS_BF16, true>(a, scale_inv, stream)
+                     : launch_store_typed<FP8TS_BF16, false>(a, 1.0f, stream);
+  }
+  return has_scale ? launch_store_typed<FP8TS_FP16, true>(a, scale_inv, stream)
+                   : launch_store_typed<FP8TS_FP16, false>(a, 1.0f, stream);
+}
 
 int launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_stride,
                     uint8_t *out, int64_t out_stride, bool has_scale, float scale_inv,

@@ -15,6 +15,11 @@
  *                    softmax, optional attention sink, bf16 output and fp32
  *                    max_logits / lse.
  *
+ * and the step upstream of them that fills the caches they read:
+ *
+ *   fp8_cache_store  quantize new K / V / index-K rows (or MLA latent + rope
+ *                    rows) and scatter them into the paged e4m3 caches.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers named as device pointers must point to device memory of the
@@ -99,6 +104,50 @@ int fp8ts_abi_version(void);
 int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
                  int64_t x_row_stride, uint8_t *out, int64_t out_row_stride,
                  const float *scale, hipStream_t stream);
+
+/*
+ * fp8_cache_store - quantize new key / value / index-key rows and write them
+ * into a paged e4m3 cache: cache row = e4m3(fl32(fl32(x) * fl32(1 / scale))).
+ *
+ * The pools keep fp8 values as value / scale with None meaning unit scale and
+ * no division (sglang PR 30971 digest, implementation step 4: the K/V,
+ * index-K and fused setters default their scale to None).  A second source
+ * fills the rest of each row, which is how the MLA prefill hook packs the
+ * latent part and the rope part of a token into one fp8 cache row (sglang PR
+ * 25460 digest, implementation step 2).  Rounding, saturation and NaN as in
+ * fp8_quantize.
+ *
+ * Token n goes to slot s = slot_mapping[n]: page s / page_size, in-page
+ * offset s % page_size.  Element c of head h lands at
+ *   cache[((page * num_heads + h) * page_size + offset) * (dim + dim2) + c]
+ * (x for c < dim, x2 for dim <= c < dim + dim2).  This covers the block-mode
+ * K/V caches [pages, Hkv, page_size, 128], the single-head index-K cache
+ * (num_heads 1) and the flat MLA KV array [S, 576] (num_heads 1,
+ * page_size 1, x = latent 512, x2 = rope 64).
+ *
+ * x               device, dtype x_dtype; element (n, h, c) at
+ *                 x[n * x_token_stride + h * x_head_stride + c] (strides in
+ *                 elements; e.g. the K part of a fused QKV projection).
+ * x2              device or NULL; same dtype; (n, h, c) at
+ *                 x2[n * x2_token_stride + h * x2_head_stride + c].  NULL
+ *                 exactly when dim2 == 0.
+ * slot_mapping    device int64 [num_tokens].  Negative slots (padding) and
+ *                 slots >= num_pages * page_size are skipped.  A slot may
+ *                 appear at most once per call (otherwise which token's row
+ *                 survives is unspecified).
+ * cache           device e4m3 [num_pages, num_heads, page_size, dim + dim2];
+ *                 bytes of slots not named are left unchanged (the cache is
+ *                 both read-modify-written state and the output).
+ * scale           host, NULL (None) or one finite float > 0.
+ * num_tokens == 0 is a no-op.
+ * Errors: FP8TS_EINVAL for null pointers, bad sizes, an unknown dtype, a bad
+ * scale, source strides that overlap rows, or a cache overlapping a source.
+ */
+int fp8_cache_store(const void *x, const void *x2, int32_t x_dtype, int64_t num_tokens,
+                    int32_t num_heads, int32_t dim, int32_t dim2, int64_t x_token_stride,
+                    int64_t x_head_stride, int64_t x2_token_stride, int64_t x2_head_stride,
+                    const int64_t *slot_mapping, uint8_t *cache, int64_t num_pages,
+                    int32_t page_size, const float *scale, hipStream_t stream);
 
 /*
  * indexer_topk - ascending top-k block ids of the lightning indexer.

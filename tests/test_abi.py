@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8ts_last_error",
+    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8ts_last_error",
               "indexer_topk_workspace_size", "sparse_attn_workspace_size", "fp8ts_abi_version"):
         assert n in names
 
@@ -82,6 +82,35 @@ def test_quantize_validation(lib):
     # empty tensors are a no-op that never touches the GPU
     assert q(lib, rows=0) == 0
     assert q(lib, cols=0, x=None, out=None) == 0
+
+
+# ----------------------------------------------------------- fp8_cache_store
+def cs(lib, **kw):
+    a = dict(x=FAKE, x2=None, dt=0, n=8, h=2, d=128, d2=0, xts=256, xhs=128, x2ts=0, x2hs=0,
+             slots=ctypes.c_void_p(0x20000000), cache=ctypes.c_void_p(0x40000000), pages=4, page=128, scale=None)
+    a.update(kw)
+    return lib.fp8_cache_store(a["x"], a["x2"], a["dt"], a["n"], a["h"], a["d"], a["d2"], a["xts"], a["xhs"],
+                               a["x2ts"], a["x2hs"], a["slots"], a["cache"], a["pages"], a["page"], a["scale"],
+                               None)
+
+
+def test_cache_store_validation(lib):
+    assert cs(lib, dt=3) == EINVAL and "x_dtype" in last(lib)
+    assert cs(lib, n=-1) == EINVAL
+    assert cs(lib, h=0) == EINVAL
+    assert cs(lib, page=0) == EINVAL
+    assert cs(lib, d2=64) == EINVAL and "x2" in last(lib)            # dim2 > 0 without x2
+    assert cs(lib, x2=FAKE2) == EINVAL and "x2" in last(lib)         # x2 with dim2 == 0
+    assert cs(lib, scale=sc(0.0)) == EINVAL and "scale" in last(lib)
+    assert cs(lib, scale=sc(float("nan"))) == EINVAL
+    assert cs(lib, xhs=64) == EINVAL and "strides" in last(lib)      # heads overlap
+    assert cs(lib, xts=200) == EINVAL and "strides" in last(lib)     # tokens overlap
+    assert cs(lib, x=None) == EINVAL
+    assert cs(lib, pages=0) == EINVAL
+    assert cs(lib, cache=ctypes.c_void_p(0x1000 + 64)) == EINVAL and "overlap" in last(lib)
+    assert cs(lib, n=1 << 30) == EUNSUP and "2^31" in last(lib)      # 32-bit chunk indexing
+    # a head stride is irrelevant with one head; an empty call launches nothing
+    assert cs(lib, n=0, x=None, cache=None) == 0
 
 
 # ----------------------------------------------------------- indexer_topk
