@@ -159,6 +159,44 @@ def measure_cache_store(fts, wl, block: bool, reps: int) -> dict:
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
+def measure_rope_quantize(fts, Q, reps: int) -> dict:
+    """fp8_rope_quantize of the MLA queries: no-rope part 512 + rope part 64
+    (rotate-half, RoFormer angles, positions 0..T-1), HBM-bound.
+
+    Algorithmic bytes: 2 read + 1 written per element, plus 8 per position
+    and the fp32 cos/sin rows of the T positions.  The same 512 MiB read
+    flush as the cache store runs between repetitions.
+    """
+    import torch
+    T, H, D = Q.shape
+    R = D - 512
+    i = np.arange(R // 2, dtype=np.float64)
+    ang = np.arange(T, dtype=np.float64)[:, None] * 10000.0 ** (-2.0 * i / R)[None, :]
+    cache = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).cuda()
+    pos = torch.arange(T, dtype=torch.int64, device="cuda")
+    out = torch.empty((T, H, D), dtype=torch.uint8, device="cuda")
+    nbytes = 3 * Q.numel() + 8 * T + 4 * T * R
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+
+    def run():
+        fts.fp8_rope_quantize(Q[..., 512:], cache, pos, x_nope=Q[..., :512], out=out)
+
+    run()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.mean(times))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -338,6 +376,8 @@ def main():
     }
 
     result["cache_store"] = measure_cache_store(fts, wl, block, args.steps)
+    if not block:
+        result["rope_quantize"] = measure_rope_quantize(fts, Q, args.steps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, block)

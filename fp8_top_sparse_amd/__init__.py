@@ -10,6 +10,7 @@ Functions (same names as the C ABI in ``include/fp8ts.h``):
 * :func:`indexer_topk`     lightning-indexer ascending top-k block ids.
 * :func:`sparse_attn_fwd`  sparse attention forward (token or block mode).
 * :func:`fp8_cache_store`  quantize new K / V / index-K rows into a paged e4m3 cache.
+* :func:`fp8_rope_quantize` RoPE fused with e4m3 quantization of Q or K.
 
 fp8 tensors are exchanged as ``torch.uint8`` holding e4m3fn bytes
 (``torch.float8_e4m3fn`` inputs are accepted and viewed as bytes).
@@ -48,6 +49,8 @@ _SIGNATURES = {
                       _fp, _fp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "fp8_cache_store": ([_vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _i32,
                          _fp, _vp], ctypes.c_int),
+    "fp8_rope_quantize": ([_vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i32,
+                           _vp, _i64, _i64, _fp, _vp], ctypes.c_int),
     "sparse_attn_workspace_size": ([_i32] * 10, _sz),
     "sparse_attn_fwd": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp, _vp,
@@ -337,5 +340,48 @@ def fp8_cache_store(x: torch.Tensor, slot_mapping: torch.Tensor, cache: torch.Te
     return cache
 
 
-__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "load", "flatten_to_2d", "EXPORTED",
+def fp8_rope_quantize(x_pe: torch.Tensor, cos_sin_cache: torch.Tensor, positions: torch.Tensor, *,
+                      x_nope: Optional[torch.Tensor] = None, is_neox: bool = True,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """e4m3 rows ``[N, H, nope + rope]`` = quantize(x_nope) ++ quantize(rope(x_pe)).
+
+    x_pe ``[N, H, R]``, ``[N, 1, R]`` or ``[N, R]`` (the last two: one rope head
+    shared by all heads); x_nope ``[N, H, nope]`` or None; cos_sin_cache fp32
+    ``[max_position, R]`` (cosines then sines); positions int64 ``[N]``.
+    """
+    lib = load()
+    if x_pe.dtype == torch.bfloat16:
+        dt = BF16
+    elif x_pe.dtype == torch.float16:
+        dt = FP16
+    else:
+        raise ValueError(f"x_pe must be bf16 or fp16, got {x_pe.dtype}")
+    n, hp, r, pts, phs = _token_head_view(x_pe, "x_pe")
+    nope, nts, nhs, h = 0, 0, 0, hp
+    if x_nope is not None:
+        if x_nope.dtype != x_pe.dtype:
+            raise ValueError("x_nope must have the dtype of x_pe")
+        n2, h, nope, nts, nhs = _token_head_view(x_nope, "x_nope")
+        if n2 != n or hp not in (1, h):
+            raise ValueError("x_nope and x_pe disagree on tokens / heads")
+    if hp == 1:
+        phs = 0                                   # one rope head, broadcast
+    if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 or not cos_sin_cache.is_contiguous() \
+            or cos_sin_cache.shape[1] != r:
+        raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, rope_dim] tensor")
+    if positions.dtype != torch.int64 or not positions.is_contiguous() or positions.numel() != n:
+        raise ValueError("positions must be a contiguous int64 tensor with one position per token")
+    if out is None:
+        out = torch.empty((n, h, nope + r), dtype=torch.uint8, device=x_pe.device)
+    ob = _bytes(out)
+    if ob.dim() != 3 or tuple(ob.shape) != (n, h, nope + r) or ob.stride(-1) != 1:
+        raise ValueError(f"out must be [N, H, {nope + r}] with a contiguous last dim")
+    _check(lib.fp8_rope_quantize(_ptr(x_nope), _ptr(x_pe), dt, n, h, nope, r, nts, nhs, pts, phs,
+                                 _ptr(cos_sin_cache), cos_sin_cache.shape[0], _ptr(positions), int(bool(is_neox)),
+                                 _ptr(ob), ob.stride(0), ob.stride(1), _scale(scale), _stream(stream)))
+    return out
+
+
+__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize", "load", "flatten_to_2d", "EXPORTED",
            "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

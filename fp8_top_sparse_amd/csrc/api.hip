@@ -134,6 +134,80 @@ int fp8_cache_store(const void *x, const void *x2, int32_t x_dtype, int64_t num_
   return launch_cache_store(a, x_dtype, has, inv, stream);
 }
 
+int fp8_rope_quantize(const void *x_nope, const void *x_pe, int32_t x_dtype, int64_t num_tokens,
+                      int32_t num_heads, int32_t nope_dim, int32_t rope_dim,
+                      int64_t nope_token_stride, int64_t nope_head_stride, int64_t pe_token_stride,
+                      int64_t pe_head_stride, const float *cos_sin_cache, int64_t max_position,
+                      const int64_t *positions, int32_t is_neox, uint8_t *out,
+                      int64_t out_token_stride, int64_t out_head_stride, const float *scale,
+                      hipStream_t stream) {
+  const char *fn = "fp8_rope_quantize";
+  if (x_dtype != FP8TS_BF16 && x_dtype != FP8TS_FP16)
+    return fail(FP8TS_EINVAL, "%s: x_dtype must be 0 (bf16) or 1 (fp16), got %d", fn, x_dtype);
+  if (num_tokens < 0 || max_position < 0) return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  if (num_heads < 1 || nope_dim < 0 || rope_dim < 2 || rope_dim % 2)
+    return fail(FP8TS_EINVAL, "%s: need num_heads >= 1, nope_dim >= 0 and an even rope_dim >= 2 (got %d, %d, %d)",
+                fn, num_heads, nope_dim, rope_dim);
+  if ((nope_dim > 0) != (x_nope != nullptr))
+    return fail(FP8TS_EINVAL, "%s: x_nope must be given exactly when nope_dim > 0", fn);
+  if (nope_dim % 8 || rope_dim % 16)
+    return fail(FP8TS_EUNSUPPORTED, "%s: nope_dim must be a multiple of 8 and rope_dim of 16 (got %d, %d)", fn,
+                nope_dim, rope_dim);
+  bool has = false;
+  float sv = 1.0f;
+  if (int st = read_scale(fn, "scale", scale, &has, &sv)) return st;
+  if (num_tokens == 0) return FP8TS_OK;
+  if (!x_pe || !cos_sin_cache || !positions || !out) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (max_position == 0) return fail(FP8TS_EINVAL, "%s: empty cos_sin_cache", fn);
+  const int64_t row = (int64_t)nope_dim + rope_dim;
+  if (num_tokens * num_heads * row >= ((int64_t)1 << 31))
+    return fail(FP8TS_EUNSUPPORTED, "%s: more than 2^31 - 1 elements in one call", fn);
+  // source rows may be read by several heads (a shared rope head has stride 0); output rows must not overlap
+  if (out_head_stride < row && num_heads > 1) return fail(FP8TS_EINVAL, "%s: out_head_stride %lld < row %lld", fn, (long long)out_head_stride, (long long)row);
+  if (num_tokens > 1 && out_token_stride < (int64_t)(num_heads - 1) * out_head_stride + row)
+    return fail(FP8TS_EINVAL, "%s: out_token_stride %lld overlaps rows", fn, (long long)out_token_stride);
+  if (nope_token_stride < 0 || nope_head_stride < 0 || pe_token_stride < 0 || pe_head_stride < 0 ||
+      out_token_stride < 0 || out_head_stride < 0)
+    return fail(FP8TS_EINVAL, "%s: negative stride", fn);
+  const bool aligned =
+      (uintptr_t)x_pe % 16 == 0 && pe_token_stride % 8 == 0 && pe_head_stride % 8 == 0 &&
+      (uintptr_t)cos_sin_cache % 16 == 0 && (uintptr_t)out % 8 == 0 && out_token_stride % 8 == 0 &&
+      out_head_stride % 8 == 0 &&
+      (nope_dim == 0 || ((uintptr_t)x_nope % 16 == 0 && nope_token_stride % 8 == 0 && nope_head_stride % 8 == 0));
+  if (!aligned)
+    return fail(FP8TS_EUNSUPPORTED, "%s: sources and cos_sin_cache need 16-byte alignment, out 8-byte, and every stride a multiple of 8", fn);
+  const size_t ob = (size_t)((num_tokens - 1) * out_token_stride + (int64_t)(num_heads - 1) * out_head_stride + row);
+  const size_t pb = (size_t)((num_tokens - 1) * pe_token_stride + (int64_t)(num_heads - 1) * pe_head_stride + rope_dim) * 2;
+  if (overlaps(out, ob, x_pe, pb)) return fail(FP8TS_EINVAL, "%s: out overlaps x_pe", fn);
+  if (nope_dim > 0) {
+    const size_t nb = (size_t)((num_tokens - 1) * nope_token_stride + (int64_t)(num_heads - 1) * nope_head_stride + nope_dim) * 2;
+    if (overlaps(out, ob, x_nope, nb)) return fail(FP8TS_EINVAL, "%s: out overlaps x_nope", fn);
+  }
+  if (overlaps(out, ob, cos_sin_cache, (size_t)(max_position * rope_dim * 4)))
+    return fail(FP8TS_EINVAL, "%s: out overlaps cos_sin_cache", fn);
+  if (overlaps(out, ob, positions, (size_t)num_tokens * 8)) return fail(FP8TS_EINVAL, "%s: out overlaps positions", fn);
+  RopeArgs a{};
+  a.x_nope = static_cast<const uint16_t *>(x_nope);
+  a.x_pe = static_cast<const uint16_t *>(x_pe);
+  a.nope_ts = nope_token_stride;
+  a.nope_hs = nope_head_stride;
+  a.pe_ts = pe_token_stride;
+  a.pe_hs = pe_head_stride;
+  a.cos_sin = cos_sin_cache;
+  a.positions = positions;
+  a.out = out;
+  a.out_ts = out_token_stride;
+  a.out_hs = out_head_stride;
+  a.num_tokens = num_tokens;
+  a.max_position = max_position;
+  a.heads = num_heads;
+  a.nope = nope_dim;
+  a.rope = rope_dim;
+  a.neox = is_neox != 0;
+  const float inv = has ? 1.0f / sv : 1.0f;   // fp32 reciprocal, rounded once
+  return launch_rope_quantize(a, x_dtype, has, inv, stream);
+}
+
 size_t indexer_topk_workspace_size(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
   if (total_q <= 0 || num_heads <= 0 || max_blocks <= 0) return 0;
   return indexer_workspace_bytes(total_q, num_heads, max_blocks);

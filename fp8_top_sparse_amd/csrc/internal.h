@@ -32,6 +32,21 @@ struct StoreArgs {
 int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scale_inv,
                        hipStream_t stream);
 
+// ---- RoPE + quantize
+struct RopeArgs {
+  const uint16_t *x_nope, *x_pe;     // [N, heads, nope] / [N, heads or 1, rope]
+  int64_t nope_ts, nope_hs, pe_ts, pe_hs;  // strides in elements (pe_hs 0: shared rope head)
+  const float *cos_sin;              // [max_position, rope]: cosines then sines
+  const int64_t *positions;          // [N]
+  uint8_t *out;                      // row (n, h) at out + n * out_ts + h * out_hs, nope + rope bytes
+  int64_t out_ts, out_hs;
+  int64_t num_tokens, max_position;
+  int32_t heads, nope, rope;
+  bool neox;
+};
+int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float scale_inv,
+                         hipStream_t stream);
+
 // ---- indexer
 struct IndexerArgs {
   const uint8_t *idx_q;

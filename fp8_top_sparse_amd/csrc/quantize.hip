@@ -168,31 +168,9 @@ int launch_typed(const uint16_t *x, int64_t rows, int64_t cols, int64_t xs, uint
 // adjacent threads, so each cache row is written as one contiguous run.
 // Index arithmetic is 32-bit (the host keeps chunk and slot counts below
 // 2^31); only byte offsets into the cache are formed in 64 bits.  Each thread
-// issues the loads of two chunks before converting either.
-template <bool VEC>
-__device__ __forceinline__ bool locate(const StoreArgs &a, uint32_t g, uint32_t cpr, uint32_t c1,
-                                       const uint16_t *&src, uint8_t *&dst) {
-  constexpr uint32_t per = VEC ? 8 : 1;
-  const uint32_t r = g / cpr;
-  const uint32_t c = g - r * cpr;
-  const uint32_t n = r / (uint32_t)a.heads;
-  const uint32_t h = r - n * (uint32_t)a.heads;
-  const int64_t slot = a.slots[n];
-  if (slot < 0 || slot >= a.num_slots) return false;
-  const uint32_t page = (uint32_t)slot / (uint32_t)a.page_size;
-  const uint32_t off = (uint32_t)slot - page * (uint32_t)a.page_size;
-  const int64_t row = a.dim + a.dim2;
-  dst = a.cache + (((int64_t)page * a.heads + h) * a.page_size + off) * row;
-  if (c < c1) {
-    src = a.x + (int64_t)n * a.x_ts + (int64_t)h * a.x_hs + c * per;
-    dst += c * per;
-  } else {
-    src = a.x2 + (int64_t)n * a.x2_ts + (int64_t)h * a.x2_hs + (c - c1) * per;
-    dst += a.dim + (c - c1) * per;
-  }
-  return true;
-}
-
+// takes two chunks and issues both source loads before it reads either slot:
+// the source address does not depend on the slot, so the two loads and the
+// slot reads are all in flight together.
 template <int DT, bool HAS_SCALE, bool VEC>
 __global__ __launch_bounds__(256) void cache_store_kernel(StoreArgs a, float s) {
   constexpr uint32_t per = VEC ? 8 : 1;
@@ -200,20 +178,47 @@ __global__ __launch_bounds__(256) void cache_store_kernel(StoreArgs a, float s) 
   const uint32_t cpr = c1 + (uint32_t)a.dim2 / per;
   const uint32_t total = (uint32_t)a.num_tokens * (uint32_t)a.heads * cpr;
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += 2 * stride) {
-    const uint16_t *s0 = nullptr, *s1 = nullptr;
-    uint8_t *d0 = nullptr, *d1 = nullptr;
-    const bool k0 = locate<VEC>(a, g, cpr, c1, s0, d0);
-    const bool k1 = g + stride < total && locate<VEC>(a, g + stride, cpr, c1, s1, d1);
-    if constexpr (VEC) {
-      v4u w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-      if (k0) w0 = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(s0));
-      if (k1) w1 = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(s1));
-      if (k0) *reinterpret_cast<v2u *>(d0) = quant8<DT, HAS_SCALE>(w0, s);
-      if (k1) *reinterpret_cast<v2u *>(d1) = quant8<DT, HAS_SCALE>(w1, s);
-    } else {
-      if (k0) *d0 = quant1<DT, HAS_SCALE>(*s0, s);
-      if (k1) *d1 = quant1<DT, HAS_SCALE>(*s1, s);
+  const int64_t row = a.dim + a.dim2;
+  for (uint32_t g0 = blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += 2 * stride) {
+    bool live[2];
+    uint32_t n[2], h[2], col[2];
+    v4u w[2];
+    uint16_t e[2];
+    int64_t slot[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      live[k] = k == 0 || g0 + stride < total;
+      const uint32_t g = live[k] ? g0 + k * stride : g0;   // a dead second chunk re-reads the first, never stored
+      const uint32_t r = g / cpr;
+      const uint32_t c = g - r * cpr;
+      n[k] = r / (uint32_t)a.heads;
+      h[k] = r - n[k] * (uint32_t)a.heads;
+      const uint16_t *src;
+      if (c < c1) {
+        src = a.x + (int64_t)n[k] * a.x_ts + (int64_t)h[k] * a.x_hs + c * per;
+        col[k] = c * per;
+      } else {
+        src = a.x2 + (int64_t)n[k] * a.x2_ts + (int64_t)h[k] * a.x2_hs + (c - c1) * per;
+        col[k] = a.dim + (c - c1) * per;
+      }
+      if constexpr (VEC) {
+        w[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src));
+      } else {
+        e[k] = *src;
+      }
+      slot[k] = a.slots[n[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!live[k] || slot[k] < 0 || slot[k] >= a.num_slots) continue;
+      const uint32_t page = (uint32_t)slot[k] / (uint32_t)a.page_size;
+      const uint32_t off = (uint32_t)slot[k] - page * (uint32_t)a.page_size;
+      uint8_t *dst = a.cache + (((int64_t)page * a.heads + h[k]) * a.page_size + off) * row + col[k];
+      if constexpr (VEC) {
+        *reinterpret_cast<v2u *>(dst) = quant8<DT, HAS_SCALE>(w[k], s);
+      } else {
+        *dst = quant1<DT, HAS_SCALE>(e[k], s);
+      }
     }
   }
 }
@@ -238,7 +243,179 @@ int launch_store_typed(const StoreArgs &a, float s, hipStream_t stream) {
   return check_launch("fp8_cache_store");
 }
 
+// ---- RoPE fused with quantization.
+//
+// Row (n, h) of the output = e4m3(x_nope[n, h, :]) ++ e4m3(rope(x_pe[n, h, :]))
+// with the rotary embedding of RoFormer at position positions[n]: the rope
+// dims form pairs (a, b) -> (a cos - b sin, b cos + a sin), pairing dim i with
+// i + R/2 (rotate-half, is_neox) or dims 2i and 2i+1 (interleaved); pair i
+// reads cos_sin_cache[p][i] and cos_sin_cache[p][R/2 + i].  This is the
+// fused rope + quantize producer of the MLA prefill hook (sglang PR 25460
+// digest, implementation step 2 and the _fused_rope_fp8_quantize excerpt),
+// with the quantize step's scale convention.  The rotation is plain fp32
+// with each product rounded on its own (no fused multiply-add), so every
+// code is decided by the same operations whatever the compiler schedules.
+// A position outside [0, max_position) writes 0x7F (NaN) over the rope part.
+//
+// HBM-bound: 2 + 1 bytes per element (the cos/sin rows of a token are read
+// once per head from cache).  One thread per 8-element output chunk.
+template <bool NEOX>
+__device__ __forceinline__ void rope8(const float *x, const float *p, const float *c,
+                                      const float *sn, bool first_half, float *o) {
+#pragma clang fp contract(off)
+  if constexpr (NEOX) {
+    // x: 8 consecutive dims of one half, p: the partner dims of the other half
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xc = x[e] * c[e];
+      const float ps = p[e] * sn[e];
+      o[e] = first_half ? xc - ps : xc + ps;
+    }
+  } else {
+    // x: 4 interleaved pairs; c, sn: their 4 angles
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = x[2 * e], b = x[2 * e + 1];
+      const float ac = a * c[e], bs = b * sn[e], bc = b * c[e], as = a * sn[e];
+      o[2 * e] = ac - bs;
+      o[2 * e + 1] = bc + as;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void widen8(v4u w, float *f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = widen<DT>(w[j] & 0xFFFF);
+    f[2 * j + 1] = widen<DT>(w[j] >> 16);
+  }
+}
+
+template <bool HAS_SCALE>
+__device__ __forceinline__ v2u encode8(const float *f, float s) {
+  uint32_t o[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    o[j] = enc2(scaled<HAS_SCALE>(f[4 * j], s), scaled<HAS_SCALE>(f[4 * j + 1], s)) |
+           (enc2(scaled<HAS_SCALE>(f[4 * j + 2], s), scaled<HAS_SCALE>(f[4 * j + 3], s)) << 16);
+  }
+  return (v2u){o[0], o[1]};
+}
+
+template <int DT, bool HAS_SCALE, bool NEOX>
+__global__ __launch_bounds__(256) void rope_quantize_kernel(RopeArgs a, float s) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  // Chunk index space: first every no-rope chunk (rows x c1), then every rope
+  // chunk (rows x c2), so a wave runs one of the two paths (a 576-wide row has
+  // 64 + 8 chunks; mixing them in one wave would pay for both).
+  const uint32_t c1 = (uint32_t)a.nope / 8;
+  const uint32_t c2 = (uint32_t)a.rope / 8;
+  const uint32_t rows = (uint32_t)a.num_tokens * (uint32_t)a.heads;
+  const uint32_t total_a = rows * c1;
+  const uint32_t total = total_a + rows * c2;
+  const uint32_t half = (uint32_t)a.rope / 2;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  // Two chunks per thread.  Source loads (and the rotate-half partner) do not
+  // depend on the position, so they are issued first; only the cos/sin rows
+  // wait for it.
+  for (uint32_t g0 = blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += 2 * stride) {
+    bool live[2], rope[2];
+    uint32_t n[2], j0[2];
+    uint8_t *dst[2];
+    v4u w[2], pw[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      live[k] = k == 0 || g0 + stride < total;
+      const uint32_t g = live[k] ? g0 + k * stride : g0;   // a dead second chunk re-reads the first, never stored
+      rope[k] = g >= total_a;
+      const uint32_t gi = rope[k] ? g - total_a : g;
+      const uint32_t cw = rope[k] ? c2 : c1;
+      const uint32_t r = gi / cw;
+      const uint32_t c = gi - r * cw;
+      n[k] = r / (uint32_t)a.heads;
+      const uint32_t h = r - n[k] * (uint32_t)a.heads;
+      dst[k] = a.out + (int64_t)n[k] * a.out_ts + (int64_t)h * a.out_hs + (rope[k] ? a.nope : 0) + c * 8;
+      j0[k] = c * 8;
+      const uint16_t *pe = a.x_pe + (int64_t)n[k] * a.pe_ts + (int64_t)h * a.pe_hs;
+      const uint16_t *src = rope[k] ? pe + j0[k] : a.x_nope + (int64_t)n[k] * a.nope_ts + (int64_t)h * a.nope_hs + j0[k];
+      w[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src));
+      if (NEOX && rope[k]) {
+        pw[k] = *reinterpret_cast<const v4u *>(pe + (j0[k] < half ? j0[k] + half : j0[k] - half));
+      } else {
+        pw[k] = w[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!live[k]) continue;
+      if (!rope[k]) {
+        *reinterpret_cast<v2u *>(dst[k]) = quant8<DT, HAS_SCALE>(w[k], s);
+        continue;
+      }
+      const int64_t pos = a.positions[n[k]];
+      if (pos < 0 || pos >= a.max_position) {
+        *reinterpret_cast<v2u *>(dst[k]) = (v2u){0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        continue;
+      }
+      const float *cs = a.cos_sin + pos * a.rope;
+      float x[8], o[8];
+      widen8<DT>(w[k], x);
+      if constexpr (NEOX) {
+        const bool first = j0[k] < half;
+        const uint32_t i0 = first ? j0[k] : j0[k] - half;   // angle index of the chunk's first dim
+        float p[8], cv[8], sv[8];
+        widen8<DT>(pw[k], p);
+        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0), cb = *reinterpret_cast<const v4f *>(cs + i0 + 4);
+        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0),
+                  sb = *reinterpret_cast<const v4f *>(cs + half + i0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cv[e] = ca[e];
+          cv[e + 4] = cb[e];
+          sv[e] = sa[e];
+          sv[e + 4] = sb[e];
+        }
+        rope8<true>(x, p, cv, sv, first, o);
+      } else {
+        const uint32_t i0 = j0[k] / 2;
+        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0);
+        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0);
+        float cv[4] = {ca[0], ca[1], ca[2], ca[3]}, sv[4] = {sa[0], sa[1], sa[2], sa[3]};
+        rope8<false>(x, nullptr, cv, sv, false, o);
+      }
+      *reinterpret_cast<v2u *>(dst[k]) = encode8<HAS_SCALE>(o, s);
+    }
+  }
+}
+
+template <int DT, bool HAS_SCALE>
+int launch_rope_typed(const RopeArgs &a, float s, hipStream_t stream) {
+  const int64_t total = a.num_tokens * a.heads * ((a.nope + a.rope) / 8);
+  int64_t blocks = (total + 511) / 512;      // two chunks per thread
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (a.neox) {
+    hipLaunchKernelGGL((rope_quantize_kernel<DT, HAS_SCALE, true>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, s);
+  } else {
+    hipLaunchKernelGGL((rope_quantize_kernel<DT, HAS_SCALE, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, s);
+  }
+  return check_launch("fp8_rope_quantize");
+}
+
 }  // namespace
+
+int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float scale_inv,
+                         hipStream_t stream) {
+  if (dtype == FP8TS_BF16) {
+    return has_scale ? launch_rope_typed<FP8TS_BF16, true>(a, scale_inv, stream)
+                     : launch_rope_typed<FP8TS_BF16, false>(a, 1.0f, stream);
+  }
+  return has_scale ? launch_rope_typed<FP8TS_FP16, true>(a, scale_inv, stream)
+                   : launch_rope_typed<FP8TS_FP16, false>(a, 1.0f, stream);
+}
 
 int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scale_inv,
                        hipStream_t stream) {

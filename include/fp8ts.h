@@ -15,10 +15,12 @@
  *                    softmax, optional attention sink, bf16 output and fp32
  *                    max_logits / lse.
  *
- * and the step upstream of them that fills the caches they read:
+ * and two producers upstream of them:
  *
- *   fp8_cache_store  quantize new K / V / index-K rows (or MLA latent + rope
- *                    rows) and scatter them into the paged e4m3 caches.
+ *   fp8_rope_quantize  rotary position embedding fused with the quantization
+ *                      of Q or K (no-rope part ++ rotated rope part per row).
+ *   fp8_cache_store    quantize new K / V / index-K rows (or MLA latent + rope
+ *                      rows) and scatter them into the paged e4m3 caches.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -104,6 +106,50 @@ int fp8ts_abi_version(void);
 int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
                  int64_t x_row_stride, uint8_t *out, int64_t out_row_stride,
                  const float *scale, hipStream_t stream);
+
+/*
+ * fp8_rope_quantize - rotary position embedding fused with e4m3 quantization,
+ * writing each head's no-rope part and rotated rope part as one fp8 row:
+ *   out[n, h] = e4m3(x_nope[n, h] * inv) ++ e4m3(rope(x_pe[n, h], positions[n]) * inv)
+ * with inv = fl32(1 / scale) (None: no multiply).
+ *
+ * This is the fused producer of the MLA prefill hook: rope and quantize Q or
+ * K and emit contiguous fp8 rows the attention kernel reads directly, with a
+ * rope part shared by all heads broadcast to every head (sglang PR 25460
+ * digest, implementation step 2 and the _fused_rope_fp8_quantize excerpt).
+ * RoPE is RoFormer's rotary embedding: the rope dims form pairs, pair i at
+ * position p turns by the angle whose cosine and sine are
+ * cos_sin_cache[p][i] and cos_sin_cache[p][rope_dim/2 + i]:
+ *   (a, b) -> (fl32(fl32(a cos) - fl32(b sin)), fl32(fl32(b cos) + fl32(a sin)))
+ * (every product rounded on its own; no fused multiply-add).  is_neox != 0
+ * pairs dim i with dim i + rope_dim/2 (rotate-half); 0 pairs dims 2i, 2i+1.
+ * Rounding, saturation and NaN as in fp8_quantize.
+ *
+ * x_nope          device or NULL (exactly when nope_dim == 0), dtype x_dtype;
+ *                 (n, h, c) at x_nope[n * nope_token_stride + h * nope_head_stride + c].
+ * x_pe            device, dtype x_dtype; (n, h, c) at
+ *                 x_pe[n * pe_token_stride + h * pe_head_stride + c];
+ *                 pe_head_stride 0 shares one rope head across all heads.
+ * cos_sin_cache   device fp32 [max_position, rope_dim] (cosines, then sines).
+ * positions       device int64 [num_tokens].  A position outside
+ *                 [0, max_position) writes 0x7F (NaN) over that token's rope
+ *                 bytes; its no-rope bytes are written as usual.
+ * out             device e4m3; row (n, h) of nope_dim + rope_dim bytes at
+ *                 out + n * out_token_stride + h * out_head_stride.
+ * Strides are in elements of the source (bytes for out).
+ * nope_dim a multiple of 8, rope_dim of 16; sources and cos_sin_cache 16-byte
+ * aligned, out 8-byte aligned, every stride a multiple of 8
+ * (FP8TS_EUNSUPPORTED otherwise).  num_tokens == 0 is a no-op.
+ * Errors: FP8TS_EINVAL for null pointers, bad sizes, an odd rope_dim, a bad
+ * scale, overlapping output rows, or an output overlapping an input.
+ */
+int fp8_rope_quantize(const void *x_nope, const void *x_pe, int32_t x_dtype, int64_t num_tokens,
+                      int32_t num_heads, int32_t nope_dim, int32_t rope_dim,
+                      int64_t nope_token_stride, int64_t nope_head_stride, int64_t pe_token_stride,
+                      int64_t pe_head_stride, const float *cos_sin_cache, int64_t max_position,
+                      const int64_t *positions, int32_t is_neox, uint8_t *out,
+                      int64_t out_token_stride, int64_t out_head_stride, const float *scale,
+                      hipStream_t stream);
 
 /*
  * fp8_cache_store - quantize new key / value / index-key rows and write them

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8ts_last_error",
+    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
+              "fp8ts_last_error",
               "indexer_topk_workspace_size", "sparse_attn_workspace_size", "fp8ts_abi_version"):
         assert n in names
 
@@ -111,6 +112,36 @@ def test_cache_store_validation(lib):
     assert cs(lib, n=1 << 30) == EUNSUP and "2^31" in last(lib)      # 32-bit chunk indexing
     # a head stride is irrelevant with one head; an empty call launches nothing
     assert cs(lib, n=0, x=None, cache=None) == 0
+
+
+# ----------------------------------------------------------- fp8_rope_quantize
+def rq(lib, **kw):
+    a = dict(xn=FAKE, xp=ctypes.c_void_p(0x2000), dt=0, n=8, h=16, nope=512, rope=64, nts=16 * 576, nhs=576,
+             pts=16 * 576, phs=576, cs=ctypes.c_void_p(0x10000000), maxp=4096, pos=ctypes.c_void_p(0x20000000),
+             neox=1, out=ctypes.c_void_p(0x40000000), ots=16 * 576, ohs=576, scale=None)
+    a.update(kw)
+    return lib.fp8_rope_quantize(a["xn"], a["xp"], a["dt"], a["n"], a["h"], a["nope"], a["rope"], a["nts"],
+                                 a["nhs"], a["pts"], a["phs"], a["cs"], a["maxp"], a["pos"], a["neox"], a["out"],
+                                 a["ots"], a["ohs"], a["scale"], None)
+
+
+def test_rope_quantize_validation(lib):
+    assert rq(lib, dt=5) == EINVAL and "x_dtype" in last(lib)
+    assert rq(lib, rope=63) == EINVAL and "rope_dim" in last(lib)
+    assert rq(lib, rope=0) == EINVAL
+    assert rq(lib, nope=0) == EINVAL and "x_nope" in last(lib)      # x_nope given without a no-rope part
+    assert rq(lib, nope=100) == EUNSUP and "multiple" in last(lib)
+    assert rq(lib, rope=24) == EUNSUP
+    assert rq(lib, scale=sc(-2.0)) == EINVAL and "scale" in last(lib)
+    assert rq(lib, xp=None) == EINVAL
+    assert rq(lib, maxp=0) == EINVAL
+    assert rq(lib, ohs=500) == EINVAL and "out_head_stride" in last(lib)
+    assert rq(lib, ots=576) == EINVAL and "out_token_stride" in last(lib)
+    assert rq(lib, xp=ctypes.c_void_p(0x2008)) == EUNSUP and "alignment" in last(lib)
+    assert rq(lib, pts=4) == EUNSUP
+    assert rq(lib, out=ctypes.c_void_p(0x1000)) == EINVAL and "overlaps" in last(lib)
+    assert rq(lib, n=1 << 22) == EUNSUP and "2^31" in last(lib)
+    assert rq(lib, n=0, xp=None, out=None) == 0
 
 
 # ----------------------------------------------------------- indexer_topk
