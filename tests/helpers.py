@@ -7,7 +7,7 @@ import math
 import numpy as np
 import torch
 
-# the benchmark spec tolerances for floating-point outputs
+# acceptance tolerances for floating-point outputs
 OUT_RTOL = 2e-2     # max|out - ref| <= OUT_RTOL * max|ref|
 LSE_ATOL = 1e-3     # |lse - ref| <= LSE_ATOL
 ML_TOL = 1e-3       # |max_logits - ref| <= ML_TOL * max(1, |ref|)
