@@ -137,7 +137,7 @@ def measure_cache_store(fts, wl, block: bool, reps: int) -> dict:
         n_tok = S
     elems = sum(x.numel() + (0 if x2 is None else x2.numel()) for x, x2, _, _ in jobs)
     nbytes = 3 * elems + 8 * n_tok * len(jobs)
-    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
 
     def run():
         for x, x2, cache, scale in jobs:
@@ -176,7 +176,7 @@ def measure_rope_quantize(fts, Q, reps: int) -> dict:
     pos = torch.arange(T, dtype=torch.int64, device="cuda")
     out = torch.empty((T, H, D), dtype=torch.uint8, device="cuda")
     nbytes = 3 * Q.numel() + 8 * T + 4 * T * R
-    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
 
     def run():
         fts.fp8_rope_quantize(Q[..., 512:], cache, pos, x_nope=Q[..., :512], out=out)
