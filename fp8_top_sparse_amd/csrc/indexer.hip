@@ -7,7 +7,8 @@
 //
 // Kernels:
 //  * prefill score kernel (MFMA): a workgroup owns 256 rows = a tile of query
-//    tokens x all index heads and walks the blocks its last token can see.
+//    tokens x all index heads and walks a chunk of up to 32 of the blocks its
+//    last token can see (long causal ranges are split over workgroups).
 //    Each 16 KB idx_k page is staged once in LDS (double-buffered, MFMA
 //    operand order) and shared by all rows; S^T = K * Q^T on 16x16x128 e4m3
 //    MFMA, the causal maximum over the page's 128 keys stays in registers, and
@@ -177,8 +178,16 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
 constexpr int kSWaves = 4, kSCols = 4, kSRows = kSWaves * kSCols * 16;
 constexpr int kFlush = 16;
 constexpr int kScPitch = kFlush + 1;          // floats per row of the score buffer
+// pages per workgroup: a tile's causal page range is split into chunks of
+// kSChunk pages, so the grid holds many similar workgroups instead of one
+// per tile (a 32k prompt would otherwise give 384 workgroups of 65..256 pages)
+#ifndef FP8TS_IDX_SCHUNK
+#define FP8TS_IDX_SCHUNK 32
+#endif
+constexpr int kSChunk = FP8TS_IDX_SCHUNK;
 
-__global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles) {
+__global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles,
+                                                                              int n_chunks) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kPage * kD];
   __shared__ float sc_s[kSRows * kScPitch];
   constexpr int NT = kSWaves * 64;
@@ -187,8 +196,15 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
   const int TT = kSRows / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, col = lane & 15;
 
-  const int b = blockIdx.x % a.batch;
-  const int tile = n_tiles - 1 - blockIdx.x / a.batch;        // heavy tiles first
+  // grid: x = sequence (fastest), then tile (heavy tiles first), then page
+  // chunk.  Consecutive workgroups go to the 8 XCDs in turn: with the chunk
+  // fastest, every tile's chunk c would land on the same XCD, and only the
+  // longest tiles have high chunks.
+  int bid = blockIdx.x;
+  const int b = bid % a.batch;
+  bid /= a.batch;
+  const int tile = n_tiles - 1 - bid % n_tiles;
+  const int chunk = bid / n_tiles;
   const int cu0 = min(max(a.cu_seqlens_q[b], 0), a.total_q);
   const int q_len = min(max(a.cu_seqlens_q[b + 1] - cu0, 0), a.total_q - cu0);
   const int t0 = tile * TT;
@@ -198,6 +214,11 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
   if (p_last < 0) return;
   const int nb_tile = min(p_last / kPage + 1, a.max_blocks);
   if (nb_tile <= a.topk) return;                 // every row takes the padding branch
+  // this workgroup scores pages [blk_lo, blk_hi) of the tile: scores need no
+  // reduction across pages, so a long causal row is split over workgroups
+  const int blk_lo = chunk * kSChunk;
+  const int blk_hi = min(nb_tile, blk_lo + kSChunk);
+  if (blk_lo >= blk_hi) return;
 
   v8i qb[kSCols];
   int row_p[kSCols];
@@ -259,22 +280,22 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
     }
   };
 
-  int cur_page = page_of(0), next_page = nb_tile > 1 ? page_of(1) : -1;
+  int cur_page = page_of(blk_lo), next_page = blk_lo + 1 < blk_hi ? page_of(blk_lo + 1) : -1;
   load(cur_page);
-  store(cur_page, kbuf[0]);
+  store(cur_page, kbuf[blk_lo & 1]);
   load(next_page);
   // drain the prologue loads once: otherwise the wait-count analysis makes
   // the first MFMA of every page wait for the in-flight prefetch
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  for (int blk = 0; blk < nb_tile; ++blk) {
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
     lds_barrier();             // page blk is in LDS; every wave is done with page blk - 1
     const uint8_t *ks = kbuf[blk & 1];
     const bool valid = cur_page >= 0;
-    if (blk + 1 < nb_tile) {
+    if (blk + 1 < blk_hi) {
       store(next_page, kbuf[(blk + 1) & 1]);
       cur_page = next_page;
-      next_page = blk + 2 < nb_tile ? page_of(blk + 2) : -1;
+      next_page = blk + 2 < blk_hi ? page_of(blk + 2) : -1;
       load(next_page);         // in flight during this page and the next
     }
     float mx[kSCols];
@@ -319,13 +340,13 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
         page_max(std::false_type{});
       }
     }
-    const int slot = blk % kFlush;
+    const int slot = (blk - blk_lo) % kFlush;
 #pragma unroll
     for (int c = 0; c < kSCols; ++c) {
       const float m = group4_max_swap(mx[c]);
       if (g == 0) sc_s[((wave * kSCols + c) * 16 + col) * kScPitch + slot] = m * a.sigma;
     }
-    if (slot == kFlush - 1 || blk == nb_tile - 1) {
+    if (slot == kFlush - 1 || blk == blk_hi - 1) {
       lds_barrier();           // every wave's scores of this group are in LDS
       flush(blk - slot, slot + 1);
     }
@@ -482,9 +503,10 @@ int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
   } else {
     const int TT = kSRows / H;
     const int n_tiles = (a.max_q_len + TT - 1) / TT;
-    const int64_t grid = (int64_t)a.batch * n_tiles;
+    const int n_chunks = (a.max_blocks + kSChunk - 1) / kSChunk;
+    const int64_t grid = (int64_t)n_chunks * a.batch * n_tiles;
     hipLaunchKernelGGL(indexer_score_shared_kernel, dim3((unsigned)grid), dim3(kSWaves * 64), 0, stream, a,
-                       n_tiles);
+                       n_tiles, n_chunks);
   }
   int st = check_launch("indexer_topk (score)");
   if (st) return st;
