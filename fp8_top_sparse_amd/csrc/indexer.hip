@@ -20,8 +20,8 @@
 //  * when no row can see more than k blocks (max_blocks <= k), a fill kernel
 //    writes the closed form 0 .. nb - 1, -1 ... and nothing is scored.
 //  * select kernel (wave64): one wave per (head, token) row.  The k-th largest
-//    score is found by an 8-bit radix select over order-preserving uint32 keys
-//    (four passes over a per-wave LDS histogram); ties at the threshold go to
+//    score is found by a bitwise search over order-preserving uint32 keys
+//    (32 steps of compare + ballot + popcount, no LDS); ties at the threshold go to
 //    the lower block id; the survivors are written by ordered compaction
 //    (ballot + popcount prefix), which yields ascending ids without a sort.
 //    The designs on the pages rank by pairwise comparison (an O(k^2)
@@ -360,12 +360,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // One wave per (head, token) row.  E = score slots per lane (nb <= 64 * E).
-// The k-th largest order-preserving key is found by an 8-bit radix select
-// (four passes over a per-wave 256-bin LDS histogram); ties at that key go to
-// the lower block id; ordered ballot compaction then writes the ids ascending.
+// The k-th largest order-preserving key is found bit by bit from the top: a
+// candidate threshold is kept when at least k keys reach it, each count being
+// E compares, ballots and popcounts (wave-uniform, no LDS).  Scores of one row
+// share a few exponents, so a histogram over the top key bits would send
+// nearly every key to the same bins.  Ties at that key go to the lower block
+// id; ordered ballot compaction then writes the ids ascending.
 template <int E>
 __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
-  __shared__ int hist_s[4][256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -385,6 +387,8 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     return;
   }
 
+  // empty slots hold key 0, which no candidate (always >= 1) counts; every
+  // real key is >= 1 (0 would be a NaN with every bit set)
   const float *sc = a.scores + ((int64_t)h * T + t) * a.max_blocks;
   uint32_t key[E];
 #pragma unroll
@@ -393,50 +397,19 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     key[e] = id < nb ? order_key(sc[id]) : 0u;
   }
 
-  int *hist = hist_s[wave];
-  uint32_t prefix = 0;          // digits of the k-th largest key decided so far
-  int need = k;                 // how many keys at or below the prefix are still to take
+  // largest thr with |{key >= thr}| >= k, i.e. the k-th largest key
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e * 64 + lane < nb && (key[e] & hmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // lane l owns digits 4l .. 4l+3; count the keys with larger digits
-    int c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = hist[lane * 4 + j];
-    const int mine = c[0] + c[1] + c[2] + c[3];
-    int suffix = mine;                               // sum over lanes >= this one
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_down(suffix, off, 64);
-      if (lane + off < 64) suffix += v;
-    }
-    int cum = suffix - mine;                         // keys with a digit above 4l+3
-    int digit = -1, above = 0;
-#pragma unroll
-    for (int j = 3; j >= 0; --j) {
-      if (cum < need && cum + c[j] >= need) {     // the one bin where the count crosses `need`
-        digit = lane * 4 + j;
-        above = cum;
-      }
-      cum += c[j];
-    }
-    const uint64_t who = __ballot(digit >= 0);      // exactly one lane holds the digit
-    const int src = __ffsll((unsigned long long)who) - 1;
-    digit = __shfl(digit, src, 64);
-    above = __shfl(above, src, 64);
-    prefix |= (uint32_t)digit << shift;
-    need -= above;
+    for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+    if (cnt >= k) thr = cand;
   }
-  const uint32_t thr = prefix;   // the k-th largest key; `need` ties at thr are kept
+  int above = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) above += __popcll(__ballot(key[e] > thr));
+  const int need = k - above;    // keys equal to thr that are kept (the lowest ids)
 
   // Ordered compaction: ids visited in ascending order, survivors packed in order.
   int base = 0, ties = 0;
