@@ -151,6 +151,54 @@ def test_token_mode_late_large_logits(gpu):
     assert_attention_close(got, ref, "late large logits (token)")
 
 
+# 128-head groups with at least 256 tokens keep each key list whole (one
+# workgroup per token and head group, final outputs written directly); the
+# smaller cases above split the lists and merge the partial results
+def test_token_mode_unsplit_lists_edge_cases(gpu):
+    q8, kv8, idx, sk = token_case(260, 128, 3000, 96, seed=41, with_invalid=True)
+    idx[3:9, :40] = -1                       # first tiles absent
+    idx[9, :] = -1
+    idx[9, 95] = 7                           # one key, in the last tile
+    tl = np.full(260, 96, np.int32)
+    tl[10], tl[11], tl[12], tl[13] = 0, 1, 31, 33
+    v8 = rand_codes(np.random.default_rng(42), (3000, 512))
+    got = gpu.sparse_attn_fwd(dev(q8), dev(kv8), dev(idx), sm_scale=1 / 24, mode="token", v=dev(v8),
+                              q_scale=0.8, k_scale=1.1, v_scale=0.6, attn_sink=dev(sk), topk_length=dev(tl))
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, v8=v8, q_scale=0.8, k_scale=1.1,
+                               v_scale=0.6, attn_sink=sk, topk_length=tl)
+    assert_attention_close(got, ref, "unsplit lists, edge cases")
+    out, ml, lse = (host(x) for x in got)
+    assert np.all(out[10] == 0) and np.all(np.isneginf(ml[10]))     # empty list: sink only
+
+
+def test_token_mode_unsplit_lists_late_large_logits(gpu):
+    """The exact-maximum rerun on the unsplit-list path (large logits from single exact products)."""
+    rng = np.random.default_rng(43)
+    T, Hq, S, topk = 256, 128, 2000, 96
+    q8 = rand_codes(rng, (T, Hq, 576), 2.0)
+    q8[:, :, 0] = W.e4m3_codes(rng.uniform(32, 64, (T, Hq)).astype(np.float32))
+    kv8 = rand_codes(rng, (S, 576), 0.02)
+    kv8[:, 0] = 0
+    idx = np.stack([np.concatenate([rng.choice(1000, 32, replace=False), 1000 + rng.choice(1000, topk - 32, replace=False)])
+                    for _ in range(T)]).astype(np.int32)
+    big = rng.choice(np.arange(1000, 2000), 40, replace=False)
+    kv8[big] = 0
+    kv8[big, 0] = W.e4m3_codes(rng.uniform(256, 448, 40).astype(np.float32))
+    got = run_token(gpu, q8, kv8, idx, 1 / 24)
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512)
+    assert ref[1].max() > 64 * math.log(2) + 1
+    assert_attention_close(got, ref, "late large logits (unsplit lists)")
+
+
+def test_token_mode_unsplit_lists_single_key_bitwise(gpu):
+    q8, kv8, _, _ = token_case(256, 128, 500, 64, seed=44, sink=False)
+    idx = np.full((256, 64), -1, np.int32)
+    idx[:, 37] = np.arange(256) % 500
+    out, ml, lse = (host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, v_scale=2.0))
+    want = 2.0 * TAB[kv8[idx[:, 37], :512]].astype(np.float64)
+    assert np.array_equal(out, np.broadcast_to(want[:, None, :], out.shape))
+
+
 # ------------------------------------------------------------------ GPU closed forms
 @pytest.mark.parametrize("Hq", [16, 128])
 def test_single_key_gives_v_bitwise(gpu, Hq):
