@@ -445,6 +445,23 @@ __global__ __launch_bounds__(256) void indexer_fill_kernel(IndexerArgs a) {
   for (int j = lane; j < a.topk; j += 64) out[j] = j < nb ? j : -1;
 }
 
+// The same closed form with 16-byte stores when k is a multiple of 4 (rows
+// stay 16-byte aligned): k / 4 threads per row, one store each.
+__global__ __launch_bounds__(256) void indexer_fill4_kernel(IndexerArgs a) {
+  const int per = a.topk >> 2;                     // threads per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / per;
+  const int64_t T = a.total_q;
+  if (row >= (int64_t)a.num_heads * T) return;
+  const int j0 = 4 * (int)(gid - row * per);
+  const int t = (int)(row % T);
+  const SeqInfo si = find_seq(a.cu_seqlens_q, a.seq_lens, a.batch, t);
+  const int nb = min(si.p < 0 ? 0 : si.p / kPage + 1, a.max_blocks);
+  const v4i ids = {j0 < nb ? j0 : -1, j0 + 1 < nb ? j0 + 1 : -1, j0 + 2 < nb ? j0 + 2 : -1,
+                   j0 + 3 < nb ? j0 + 3 : -1};
+  *reinterpret_cast<v4i *>(a.out_ids + row * a.topk + j0) = ids;
+}
+
 }  // namespace
 
 size_t indexer_workspace_bytes(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
@@ -460,7 +477,12 @@ int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
   if (a.max_blocks <= a.topk) {
     // no row can have more than k blocks: nothing to score or rank
     const int64_t rows = (int64_t)H * a.total_q;
-    hipLaunchKernelGGL(indexer_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    if (a.topk % 4 == 0 && (uintptr_t)a.out_ids % 16 == 0) {
+      const int64_t threads = rows * (a.topk / 4);
+      hipLaunchKernelGGL(indexer_fill4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(indexer_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    }
     return check_launch("indexer_topk (closed form)");
   }
   const bool small = (int64_t)a.max_q_len * H <= 16;
