@@ -257,3 +257,54 @@ def test_binding_maps_status_to_python_errors(lib):
         fts._check(EINVAL)
     with pytest.raises(fts.Fp8tsError):
         fts._check(3)
+
+
+# ----------------------------------------------------------- the header from plain C
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "fp8ts.h"
+
+int main(void) {
+  if (fp8ts_abi_version() != 1) return 10;
+  float bad = -1.0f;
+  /* every call below fails validation on the host before any launch */
+  if (fp8_quantize((const void *)0x1000, 7, 4, 8, 8, (uint8_t *)0x100000, 8, NULL, 0) != FP8TS_EINVAL) return 11;
+  if (!strstr(fp8ts_last_error(), "x_dtype")) return 12;
+  if (fp8_quantize((const void *)0x1000, FP8TS_BF16, 4, 8, 8, (uint8_t *)0x100000, 8, &bad, 0) != FP8TS_EINVAL)
+    return 13;
+  if (indexer_topk(NULL, NULL, 1, NULL, 1, NULL, NULL, 1, 1, 1, 4, 64, 128, 0.1f, NULL, NULL, 8, NULL, NULL, 0, 0)
+      != FP8TS_EUNSUPPORTED) return 14;
+  if (fp8_cache_store((const void *)0x1000, NULL, FP8TS_BF16, 4, 1, 128, 64, 128, 128, 0, 0,
+                      (const int64_t *)0x2000, (uint8_t *)0x100000, 4, 128, NULL, 0) != FP8TS_EINVAL) return 15;
+  if (fp8_rope_quantize(NULL, (const void *)0x1000, FP8TS_BF16, 4, 1, 0, 63, 0, 0, 64, 64,
+                        (const float *)0x2000, 16, (const int64_t *)0x3000, 1, (uint8_t *)0x100000, 64, 64, NULL, 0)
+      != FP8TS_EINVAL) return 16;
+  if (sparse_attn_workspace_size(FP8TS_BLOCK_MODE, 0, 0, 0, 16, 2, 4, 128, 64, 8) != 0) return 17;
+  /* empty inputs are no-ops */
+  if (fp8_quantize(NULL, FP8TS_FP16, 0, 8, 8, NULL, 8, NULL, 0) != FP8TS_OK) return 18;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(lib, tmp_path):
+    """include/fp8ts.h is a C header: a C program built with gcc links the library
+    and gets the documented status codes (host validation only, no GPU)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are missing")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(fts.LIB_PATH)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", str(src), "-o", str(exe), f"-L{libdir}", "-l:libfp8ts.so",
+           f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "HIP_VISIBLE_DEVICES": ""})
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
