@@ -94,6 +94,22 @@ def block_attention_flops(ids: np.ndarray, pos: np.ndarray, hq: int, hidx: int, 
     return keys * (hq // hidx) * 2 * (d_qk + d_v)
 
 
+def decode_attention_bytes(ids: np.ndarray, seq: np.ndarray, hq: int, hidx: int, hkv: int, d: int) -> int:
+    """Algorithmic HBM bytes of block-mode decode attention: every (sequence, kv
+    head) reads the K and V pages of the union of its index heads' selected
+    blocks once (2 * PAGE * d bytes each), plus the e4m3 queries and the bf16
+    outputs (max_logits / lse: 8 bytes per row)."""
+    per_kv = hidx // hkv
+    pages = 0
+    for b in np.unique(seq):
+        rows = np.nonzero(seq == b)[0]
+        for kh in range(hkv):
+            sel = ids[kh * per_kv:(kh + 1) * per_kv][:, rows].ravel()
+            pages += len(np.unique(sel[sel >= 0]))
+    rows = len(seq) * hq
+    return pages * 2 * PAGE * d + rows * (d + 2 * d + 8)
+
+
 def token_positions(cu_seqlens_q, seq_lens):
     """(sequence id, absolute position) of every flattened query token."""
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -374,6 +390,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": committed_traffic(args.workload)},
     }
+    if block and wl.max_q_len == 1:
+        # decode: one query per sequence, so the attention streams the selected
+        # K/V pages and is bound by HBM, not by the matrix cores
+        seq, _ = token_positions(wl.cu_seqlens_q, wl.seq_lens)
+        dbytes = decode_attention_bytes(ids_h, seq, Hq, Hidx, Hkv, D)
+        gbps = dbytes / (ms["attn"] * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                              "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": committed_traffic(args.workload),
+                              "algorithmic_bytes": int(dbytes)}
 
     result["cache_store"] = measure_cache_store(fts, wl, block, args.steps)
     if not block:
