@@ -57,7 +57,8 @@ def calibrate_copy(mib: int) -> None:
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
 
-TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md"}
+TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md",
+                   5: "profiles/attn_block_decode__gqa_decode_b64_s32768_top64.md"}
 
 
 def kernel_source_digest() -> str:
