@@ -435,6 +435,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
 // Merge split partials: out = v_scale * sum_s O_s 2^(m_s - M) / L.
 template <int DV>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) {
+  // one workgroup per (token, head) row; thread i owns DV / 128 consecutive dims
+  constexpr int VPT = DV / 128;
+  static_assert(VPT == 1 || VPT == 4, "combine: 128 or 512 output dims");
   const int64_t rowidx = blockIdx.x;            // t * hq + h
   const int h = (int)(rowidx % a.hq);
   const int64_t TH = (int64_t)a.total_q * a.hq;
@@ -442,28 +445,40 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
   const float zs = has_sink ? a.sink_scale_log2 * a.sink[h] : -INFINITY;
   float M = zs, mtrue = -INFINITY;
   for (int s = 0; s < gr.splits; ++s) {
-    const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
+    const v4f pm = *reinterpret_cast<const v4f *>(gr.part_ml + (s * TH + rowidx) * 4);
     M = fmaxf(M, pm[0]);
     mtrue = fmaxf(mtrue, pm[2]);
   }
+  // every split's weight exp2(m_s - M) once, then the dims with 16-byte loads
   float Lt = 0.f;
+  float acc[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) acc[j] = 0.f;
+  const int d0 = threadIdx.x * VPT;
   if (M != -INFINITY) {
     for (int s = 0; s < gr.splits; ++s) {
-      const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
-      if (pm[0] != -INFINITY) Lt += pm[1] * exp2f(pm[0] - M);
+      const v4f pm = *reinterpret_cast<const v4f *>(gr.part_ml + (s * TH + rowidx) * 4);
+      if (pm[0] == -INFINITY) continue;
+      const float w = exp2f(pm[0] - M);
+      Lt += pm[1] * w;
+      const float *po = gr.part_o + (s * TH + rowidx) * DV + d0;
+      if constexpr (VPT == 4) {
+        const v4f x = *reinterpret_cast<const v4f *>(po);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += x[j] * w;
+      } else {
+        acc[0] += po[0] * w;
+      }
     }
     if (has_sink) Lt += exp2f(zs - M);
   }
   const float scale = Lt > 0.f ? a.v_scale / Lt : 0.f;
-  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
-    float acc = 0.f;
-    if (Lt > 0.f) {
-      for (int s = 0; s < gr.splits; ++s) {
-        const float *pm = gr.part_ml + (s * TH + rowidx) * 4;
-        if (pm[0] != -INFINITY) acc += gr.part_o[(s * TH + rowidx) * DV + d] * exp2f(pm[0] - M);
-      }
-    }
-    a.out[rowidx * DV + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * scale));
+  uint16_t *orow = a.out + rowidx * DV + d0;
+  if constexpr (VPT == 4) {
+    *reinterpret_cast<uint2 *>(orow) =
+        make_uint2(pack_bf16x2(acc[0] * scale, acc[1] * scale), pack_bf16x2(acc[2] * scale, acc[3] * scale));
+  } else {
+    orow[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * scale));
   }
   if (threadIdx.x == 0) {
     a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
