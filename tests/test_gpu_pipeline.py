@@ -122,3 +122,63 @@ def test_mla_prefill_layer(gpu, neox):
     ref = OA.sparse_attn_token(r_q8, r_kv8, idx, sm_scale=sm, d_v=512, q_scale=q_s, k_scale=kv_s, v_scale=kv_s,
                                attn_sink=sink)
     assert_attention_close(got, ref, "mla prefill layer")
+
+
+def test_decode_step_layer(gpu):
+    """A decode step: each sequence's new K / V / index-K stored at its last
+    position into caches already holding the prompt, then the index query and
+    Q quantized, top-8 blocks selected and attended (the new key sees itself)."""
+    rng = np.random.default_rng(79)
+    B, Hq, Hkv, Hidx, D, topk = 6, 16, 2, 4, 128, 8
+    seq_lens = np.array([1500, 1024, 129, 2047, 900, 1921], np.int32)
+    nbs = (seq_lens + PAGE - 1) // PAGE
+    mb = int(nbs.max())
+    P = int(nbs.sum()) + 3
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((B, mb), -1, np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :nbs[b]] = perm[o:o + nbs[b]]
+        o += nbs[b]
+    ints = W.E4M3_EXACT_INTS
+    ik_s, iq_s, k_s, v_s = 0.5, 4.0, 1.7, 0.6
+    # the caches already hold the prompt (all but the last position of each sequence)
+    kc0 = W.e4m3_codes((rng.standard_normal((P, Hkv, PAGE, D)) / k_s).astype(np.float32))
+    vc0 = W.e4m3_codes((rng.standard_normal((P, Hkv, PAGE, D)) / v_s).astype(np.float32))
+    ik0 = W.e4m3_codes((rng.choice(ints[ints <= 16], (P, PAGE, D)) * rng.choice([-1.0, 1.0], (P, PAGE, D)))
+                       .astype(np.float32))
+    pos = (seq_lens - 1).astype(np.int64)
+    slots = table[np.arange(B), pos // PAGE].astype(np.int64) * PAGE + pos % PAGE
+    k_b = bf16_bits(rng.standard_normal((B, Hkv, D)))
+    v_b = bf16_bits(rng.standard_normal((B, Hkv, D)))
+    ik_b = bf16_bits(rng.choice(ints[ints <= 16], (B, 1, D)) * rng.choice([-1.0, 1.0], (B, 1, D)) * ik_s)
+    q_b = bf16_bits(rng.standard_normal((B, Hq, D)))
+    iq_b = bf16_bits(rng.choice(ints, (B, Hidx, D)) * rng.choice([-1.0, 1.0], (B, Hidx, D)) * iq_s)
+    cu = np.arange(B + 1, dtype=np.int32)
+
+    kc, vc, ikc = dev(kc0), dev(vc0), dev(ik0)
+    sl_d = dev(slots)
+    gpu.fp8_cache_store(bf16_tensor(k_b), sl_d, kc, scale=k_s)
+    gpu.fp8_cache_store(bf16_tensor(v_b), sl_d, vc, scale=v_s)
+    gpu.fp8_cache_store(bf16_tensor(ik_b[:, 0]), sl_d, ikc, scale=ik_s)
+    q8 = gpu.fp8_quantize(bf16_tensor(q_b), None)
+    iq8 = gpu.fp8_quantize(bf16_tensor(iq_b), iq_s)
+    ids = gpu.indexer_topk(iq8, ikc, dev(table), dev(cu), dev(seq_lens), max_q_len=1, sm_scale=1 / math.sqrt(D),
+                           topk=topk, idx_q_scale=iq_s, idx_k_scale=ik_s)
+    got = gpu.sparse_attn_fwd(q8, kc, ids, v=vc, sm_scale=1 / math.sqrt(D), mode="block", block_table=dev(table),
+                              cu_seqlens_q=dev(cu), seq_lens=dev(seq_lens), max_q_len=1, k_scale=k_s, v_scale=v_s)
+    torch.cuda.synchronize()
+
+    r_kc = OCS.cache_store(kc0, k_b, OQ.BF16, slots, k_s)
+    r_vc = OCS.cache_store(vc0, v_b, OQ.BF16, slots, v_s)
+    r_ikc = OCS.cache_store(ik0[:, None], ik_b, OQ.BF16, slots, ik_s)[:, 0]
+    r_q8 = OQ.quantize(q_b, OQ.BF16, None)
+    r_iq8 = OQ.quantize(iq_b, OQ.BF16, iq_s)
+    r_ids = OI.indexer_topk(r_iq8, r_ikc, table, cu, seq_lens, sm_scale=1 / math.sqrt(D), topk=topk,
+                            idx_q_scale=iq_s, idx_k_scale=ik_s)
+    assert np.array_equal(kc.cpu().numpy(), r_kc) and np.array_equal(vc.cpu().numpy(), r_vc)
+    assert np.array_equal(ikc.cpu().numpy(), r_ikc)
+    assert np.array_equal(ids.cpu().numpy(), r_ids)
+    ref = OA.sparse_attn_block(r_q8, r_kc, r_vc, r_ids, table, cu, seq_lens, sm_scale=1 / math.sqrt(D),
+                               k_scale=k_s, v_scale=v_s)
+    assert_attention_close(got, ref, "decode step layer")
