@@ -61,11 +61,16 @@ TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md",
                    5: "profiles/attn_block_decode__gqa_decode_b64_s32768_top64.md"}
 
 
-def kernel_source_digest() -> str:
-    """sha256 (first 16 hex) of the attention kernel source and its build flags."""
+# the source file of the attention kernel that dominates each workload's step
+KERNEL_SOURCE = {2: "fp8_top_sparse_amd/csrc/attention_block.hip",
+                 5: "fp8_top_sparse_amd/csrc/attention_decode.hip"}
+
+
+def kernel_source_digest(workload: int) -> str:
+    """sha256 (first 16 hex) of the workload's attention kernel source and its build flags."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("fp8_top_sparse_amd/csrc/attention_block.hip", "fp8_top_sparse_amd/csrc/attn_common.h",
+    for f in (KERNEL_SOURCE[workload], "fp8_top_sparse_amd/csrc/attn_common.h",
               "fp8_top_sparse_amd/csrc/device.h", "fp8_top_sparse_amd/build.py"):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
@@ -82,7 +87,7 @@ def committed_traffic(workload: int):
     import re
     dig = re.search(r"first 16 hex\): `([0-9a-f]{16})`", text)
     val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not dig or not val or dig.group(1) != kernel_source_digest():
+    if not dig or not val or dig.group(1) != kernel_source_digest(workload):
         return None
     return int(val.group(1))
 

@@ -491,11 +491,15 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
 #define FP8TS_DECODE_CHUNK 32
 #endif
 constexpr int kDecodeChunk = FP8TS_DECODE_CHUNK;   // union blocks per decode workgroup
+#ifndef FP8TS_STREAM_CHUNK
+#define FP8TS_STREAM_CHUNK 32
+#endif
+constexpr int kStreamChunk = FP8TS_STREAM_CHUNK;   // union blocks per streamed-decode workgroup (0: off)
 
 struct Plan {
   int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads,
               // 4 block prefill, pipelined, 5 block decode, pipelined,
-              // 6 token 128 heads, pipelined
+              // 6 token 128 heads, pipelined, 7 block decode, streamed per wave
   Grid gr;
   int64_t nblocks;
   size_t lds;
@@ -557,6 +561,24 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
         pl.kind = 5;
         pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
         pl.lds = block_decode_lds(gr);
+      }
+    }
+    // decode tiles of at most 16 rows: the streamed decode kernel, every wave
+    // walking its own share of ~kStreamChunk blocks of the union
+    if (kStreamChunk > 0 && decode && gr.G <= 16 && 16 % gr.G == 0 && (int64_t)max_q_len * gr.G <= 16) {
+      Grid sg = pl.gr;
+      sg.TT = 16 / sg.G;
+      sg.n_tiles = (max_q_len + sg.TT - 1) / sg.TT;
+      sg.NL = sg.TT * sg.n_il;
+      int ubound = sg.n_il * (sg.TT < max_q_len ? sg.TT : max_q_len) * topk;
+      if (ubound > max_blocks) ubound = max_blocks;
+      sg.splits = (ubound + kStreamChunk - 1) / kStreamChunk;
+      if (sg.splits < 1) sg.splits = 1;
+      if (block_stream_decode_lds(sg) <= kMaxLds) {
+        gr = sg;
+        pl.kind = 7;
+        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+        pl.lds = block_stream_decode_lds(gr);
       }
     }
     // prefill tiles go to the pipelined kernel when its LDS fits; otherwise to
@@ -658,6 +680,7 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
     case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
     case 4: st = launch_block_prefill(a, pl.gr, pl.nblocks, stream); break;
     case 5: st = launch_block_decode(a, pl.gr, pl.nblocks, stream); break;
+    case 7: st = launch_block_stream_decode(a, pl.gr, pl.nblocks, stream); break;
     case 6:
       if (token_mla_fits(a)) {
         st = launch_token_mla(a, pl.gr, pl.nblocks, stream);

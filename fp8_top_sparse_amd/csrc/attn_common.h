@@ -242,6 +242,10 @@ int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hip
 size_t block_decode_lds(const Grid &gr);
 int block_decode_rows();
 int launch_block_decode(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
+// Block-mode decode with every wave streaming its own blocks
+// (attention_decode.hip): one 16-row tile (tokens x q heads of one kv head).
+size_t block_stream_decode_lds(const Grid &gr);
+int launch_block_stream_decode(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 // Token-mode MLA kernel with pipelined K/V tiles (attention_token.hip): 128 q
 // heads of one token per workgroup.  token_mla_fits: the caches are small
 // enough for its 32-bit byte offsets.

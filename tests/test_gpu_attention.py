@@ -435,3 +435,66 @@ def test_block_decode_full_size_sampled(gpu):
                                sm_scale=wl.sm_scale, tokens=seqs)
     out, ml, lse = got
     assert_attention_close((out[seqs], ml[seqs], lse[seqs]), ref, "decode full")
+
+
+# Decode tiles of at most 16 rows (q heads per kv head x query tokens) run the
+# streamed decode kernel, each wave walking its own share of the block union.
+@pytest.mark.parametrize("Hq,Hkv,Hidx,q_len", [(16, 2, 4, 1), (32, 2, 4, 1), (8, 8, 2, 1), (4, 2, 2, 1),
+                                               (16, 2, 4, 2), (8, 2, 2, 4), (16, 1, 16, 1)])
+def test_block_decode_streamed_head_layouts(gpu, Hq, Hkv, Hidx, q_len):
+    rng = np.random.default_rng(Hq * 100 + Hkv * 10 + q_len)
+    seq = [int(x) for x in rng.integers(q_len, 9000, 9)] + [q_len, 128, 129, 8192]
+    c = block_case(seq, [q_len] * len(seq), seed=Hq + Hidx + q_len, topk=24, Hq=Hq, Hkv=Hkv, Hidx=Hidx,
+                   sink=True)
+    got = run_block(gpu, c, q_scale=0.9, k_scale=1.1, v_scale=2.0)
+    ref = ref_block(c, q_scale=0.9, k_scale=1.1, v_scale=2.0)
+    assert_attention_close(got, ref, f"decode Hq={Hq} Hkv={Hkv} Hidx={Hidx} q_len={q_len}")
+
+
+@pytest.mark.parametrize("topk", [1, 2, 31, 32, 33, 48, 64])
+def test_block_decode_streamed_split_edges(gpu, topk):
+    """Lists just below, at and above one split's worth of blocks (and a
+    single-block list), over sequences both shorter and longer than k blocks."""
+    seq = [1, 100, 4000, 9000, 16000, 30000]
+    c = block_case(seq, [1] * len(seq), seed=topk, topk=topk)
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, f"decode k={topk}")
+
+
+def test_block_decode_streamed_empty_rows_and_absent_ids(gpu):
+    seq = [5000, 3000, 700, 12000]
+    c = block_case(seq, [1] * 4, seed=41, topk=16, sink=True)
+    c["ids"] = c["ids"].copy()
+    c["ids"][:, 1] = -1                 # a sequence that selected nothing
+    c["ids"][2, 3, :5] = 1000           # ids beyond the table: absent
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, "decode empty rows")
+    out, ml, lse = (host(x) for x in got)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(ml[1]))
+
+
+def test_block_decode_streamed_late_large_logits(gpu):
+    """Decode rows whose first selected blocks carry tiny logits and a later
+    block logits beyond fp32's range relative to them: each wave reruns its
+    share with the exact maxima (single exact products in the large block,
+    as in the prefill case above)."""
+    seq = [1500, 2000]
+    c = block_case(seq, [1, 1], seed=43, topk=12)
+    rng = np.random.default_rng(43)
+    kc = c["kc"].copy()
+    for b in range(2):
+        bt = c["bt"][b]
+        kc[bt[:8]] = rand_codes(rng, (8,) + kc.shape[1:], 0.02)
+        kc[bt[10]] = 0
+        kc[bt[10], :, :, 0] = W.e4m3_codes(rng.uniform(256, 448, kc.shape[1:3]).astype(np.float32))
+    c["kc"] = kc
+    ids = np.full((4, 2, 12), -1, np.int32)
+    ids[:, 0, :12] = np.arange(12)
+    ids[:, 1, :12] = np.arange(12)
+    c["ids"] = ids
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert ref[2].max() > 64 * math.log(2) + 5    # far beyond the tiny blocks that start each share
+    assert_attention_close(got, ref, "decode late large logits")
