@@ -377,6 +377,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
         for (int h = 0; h < 2; ++h) {
           // ---- S^T = K Q^T + C for 64 keys
           v4f s[4][kCols];
+          // The MFMA runs (QK here, PV below) issue at raised wave priority:
+          // when both waves of a SIMD are ready, the one feeding the matrix
+          // core goes first and the other's softmax VALU fills its gaps.  The
+          // priority changes also keep the exps out of the PV stream
+          // (8k prefill: 263.7 us against 271.2 us, four paired runs)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             const v8i ka = lds_read32x2(kt_s + op_lane + 1024 * (2 * (4 * h + kt)));
@@ -387,6 +393,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           sched_mfma_then_reads<2, kCols, 2>();
           sched_mfma_then_reads<2, kCols, 0>();
+          __builtin_amdgcn_s_setprio(0);
           // ---- causal mask, only where some row of the wave needs one
           const int kpos0 = key_base + 64 * h;
           bool part = false;
@@ -460,6 +467,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
             }
           }
           // ---- O^T += V^T P^T
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -475,6 +483,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           __builtin_amdgcn_sched_group_barrier(0x100, kPvAhead, 0);
           sched_mfma_then_reads<2 * kNdt - kPvAhead, kCols, 1>();
           sched_mfma_then_reads<kPvAhead, kCols, 0>();
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       if (it + 1 < n_iter) {
