@@ -19,12 +19,13 @@ indexer    lightning-indexer block scores and ascending top-k block ids.
 attention  sparse attention forward (token mode and block mode).
 cache_store  quantize new K / V / index-K rows into a paged fp8 cache.
 rope       rotary position embedding fused with e4m3 quantization.
+qknorm     per-head RMS norm + RoPE + e4m3 quantization (+ paged store) of index q / k.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against closed
 forms, exhaustive enumeration, brute force and library routines; the pin for
 each function is listed in its docstring.
 """
 
-from . import e4m3, quantize, indexer, attention, cache_store, rope  # noqa: F401
+from . import e4m3, quantize, indexer, attention, cache_store, rope, qknorm  # noqa: F401
 
-__all__ = ["e4m3", "quantize", "indexer", "attention", "cache_store", "rope"]
+__all__ = ["e4m3", "quantize", "indexer", "attention", "cache_store", "rope", "qknorm"]
