@@ -11,6 +11,8 @@ Functions (same names as the C ABI in ``include/fp8ts.h``):
 * :func:`sparse_attn_fwd`  sparse attention forward (token or block mode).
 * :func:`fp8_cache_store`  quantize new K / V / index-K rows into a paged e4m3 cache.
 * :func:`fp8_rope_quantize` RoPE fused with e4m3 quantization of Q or K.
+* :func:`fp8_qknorm_rope_quantize` per-head RMS norm + RoPE + e4m3 of the index
+  query / key, into fp8 rows and/or the paged index-K cache.
 
 fp8 tensors are exchanged as ``torch.uint8`` holding e4m3fn bytes
 (``torch.float8_e4m3fn`` inputs are accepted and viewed as bytes).
@@ -51,6 +53,8 @@ _SIGNATURES = {
                          _fp, _vp], ctypes.c_int),
     "fp8_rope_quantize": ([_vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i32,
                            _vp, _i64, _i64, _fp, _vp], ctypes.c_int),
+    "fp8_qknorm_rope_quantize": ([_vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _vp, _f32, _vp, _i64, _vp,
+                                  _i32, _vp, _i64, _i64, _vp, _vp, _i64, _i32, _fp, _vp], ctypes.c_int),
     "sparse_attn_workspace_size": ([_i32] * 10, _sz),
     "sparse_attn_fwd": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp, _vp,
@@ -383,5 +387,74 @@ def fp8_rope_quantize(x_pe: torch.Tensor, cos_sin_cache: torch.Tensor, positions
     return out
 
 
-__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize", "load", "flatten_to_2d", "EXPORTED",
+def fp8_qknorm_rope_quantize(x: torch.Tensor, norm_weight: torch.Tensor, eps: float, *, rope_dim: int = 0,
+                             cos_sin_cache: Optional[torch.Tensor] = None,
+                             positions: Optional[torch.Tensor] = None, is_neox: bool = True,
+                             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                             write_out: bool = True, slot_mapping: Optional[torch.Tensor] = None,
+                             cache: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """e4m3 rows ``[N, H, D]`` of quantize(rope_last_R(rms_norm(x) * w)).
+
+    x ``[N, H, D]`` or ``[N, D]`` bf16/fp16; norm_weight fp32 ``[D]``; the last
+    ``rope_dim`` dims are rotated (cos_sin_cache fp32 ``[max_position,
+    rope_dim]``, positions int64 ``[N]``).  With ``slot_mapping`` (int64 ``[N]``)
+    the rows are also stored into ``cache`` (e4m3 bytes ``[pages, H, page, D]``
+    or ``[pages, page, D]`` for one head).  ``write_out=False`` skips the
+    returned rows (store only); then None is returned.
+    """
+    lib = load()
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float16:
+        dt = FP16
+    else:
+        raise ValueError(f"x must be bf16 or fp16, got {x.dtype}")
+    n, h, d, xts, xhs = _token_head_view(x, "x")
+    if norm_weight.dtype != torch.float32 or not norm_weight.is_contiguous() or norm_weight.numel() != d:
+        raise ValueError(f"norm_weight must be a contiguous float32 tensor of {d} values")
+    r = int(rope_dim)
+    if r > 0:
+        if cos_sin_cache is None or positions is None:
+            raise ValueError("rope_dim > 0 needs cos_sin_cache and positions")
+        if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 or \
+                not cos_sin_cache.is_contiguous() or cos_sin_cache.shape[1] != r:
+            raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, rope_dim] tensor")
+        if positions.dtype != torch.int64 or not positions.is_contiguous() or positions.numel() != n:
+            raise ValueError("positions must be a contiguous int64 tensor with one position per token")
+    max_pos = cos_sin_cache.shape[0] if (r > 0 and cos_sin_cache is not None) else 0
+    ob = None
+    if write_out:
+        if out is None:
+            out = torch.empty((n, h, d), dtype=torch.uint8, device=x.device)
+        ob = _bytes(out)
+        if ob.dim() != 3 or tuple(ob.shape) != (n, h, d) or ob.stride(-1) != 1:
+            raise ValueError(f"out must be [N, H, {d}] with a contiguous last dim")
+    pages, page, cb = 0, 1, None
+    if slot_mapping is not None:
+        if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous() or slot_mapping.numel() != n:
+            raise ValueError("slot_mapping must be a contiguous int64 tensor with one slot per token")
+        if cache is None:
+            raise ValueError("slot_mapping needs a cache")
+        cb = _bytes(cache)
+        if not cb.is_contiguous():
+            raise ValueError("cache must be contiguous")
+        if cb.dim() == 4:
+            pages, ch, page, row = cb.shape
+        elif cb.dim() == 3:
+            (pages, page, row), ch = cb.shape, 1
+        else:
+            raise ValueError("cache must be [pages, H, page, D] or [pages, page, D]")
+        if ch != h or row != d:
+            raise ValueError(f"cache heads/row ({ch}, {row}) do not match x ({h}, {d})")
+    _check(lib.fp8_qknorm_rope_quantize(_ptr(x), dt, n, h, d, r, xts, xhs, _ptr(norm_weight), float(eps),
+                                        _ptr(cos_sin_cache) if r > 0 else None, max_pos,
+                                        _ptr(positions) if r > 0 else None, int(bool(is_neox)), _ptr(ob),
+                                        ob.stride(0) if ob is not None else 0,
+                                        ob.stride(1) if ob is not None else 0, _ptr(slot_mapping), _ptr(cb),
+                                        pages, page, _scale(scale), _stream(stream)))
+    return out if write_out else None
+
+
+__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
+           "fp8_qknorm_rope_quantize", "load", "flatten_to_2d", "EXPORTED",
            "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

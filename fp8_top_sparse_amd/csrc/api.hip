@@ -208,6 +208,94 @@ int fp8_rope_quantize(const void *x_nope, const void *x_pe, int32_t x_dtype, int
   return launch_rope_quantize(a, x_dtype, has, inv, stream);
 }
 
+int fp8_qknorm_rope_quantize(const void *x, int32_t x_dtype, int64_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t rope_dim, int64_t x_token_stride,
+                             int64_t x_head_stride, const float *norm_weight, float eps,
+                             const float *cos_sin_cache, int64_t max_position,
+                             const int64_t *positions, int32_t is_neox, uint8_t *out,
+                             int64_t out_token_stride, int64_t out_head_stride,
+                             const int64_t *slot_mapping, uint8_t *cache, int64_t num_pages,
+                             int32_t page_size, const float *scale, hipStream_t stream) {
+  const char *fn = "fp8_qknorm_rope_quantize";
+  if (x_dtype != FP8TS_BF16 && x_dtype != FP8TS_FP16)
+    return fail(FP8TS_EINVAL, "%s: x_dtype must be 0 (bf16) or 1 (fp16), got %d", fn, x_dtype);
+  if (num_tokens < 0 || max_position < 0 || num_pages < 0) return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  if (num_heads < 1 || head_dim < 1 || rope_dim < 0 || rope_dim % 2 || rope_dim > head_dim)
+    return fail(FP8TS_EINVAL, "%s: need num_heads >= 1, head_dim >= 1 and an even rope_dim in [0, head_dim] (got %d, %d, %d)",
+                fn, num_heads, head_dim, rope_dim);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(FP8TS_EINVAL, "%s: eps must be finite and >= 0 (got %g)", fn, (double)eps);
+  if (!out && !slot_mapping) return fail(FP8TS_EINVAL, "%s: neither out nor slot_mapping given", fn);
+  if (slot_mapping && page_size < 1) return fail(FP8TS_EINVAL, "%s: page_size must be >= 1 (got %d)", fn, page_size);
+  if (head_dim % 8 || head_dim > 512 || rope_dim % 16)
+    return fail(FP8TS_EUNSUPPORTED, "%s: head_dim must be a multiple of 8 up to 512 and rope_dim a multiple of 16 (got %d, %d)",
+                fn, head_dim, rope_dim);
+  bool has = false;
+  float sv = 1.0f;
+  if (int st = read_scale(fn, "scale", scale, &has, &sv)) return st;
+  if (num_tokens == 0) return FP8TS_OK;
+  if (!x || !norm_weight || (rope_dim > 0 && (!cos_sin_cache || !positions)))
+    return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (slot_mapping && !cache) return fail(FP8TS_EINVAL, "%s: slot_mapping given without a cache", fn);
+  if (rope_dim > 0 && max_position == 0) return fail(FP8TS_EINVAL, "%s: empty cos_sin_cache", fn);
+  if (slot_mapping && num_pages == 0) return fail(FP8TS_EINVAL, "%s: empty cache", fn);
+  if (num_tokens * num_heads * head_dim >= ((int64_t)1 << 31))
+    return fail(FP8TS_EUNSUPPORTED, "%s: more than 2^31 - 1 elements in one call", fn);
+  if (x_token_stride < 0 || x_head_stride < 0 || out_token_stride < 0 || out_head_stride < 0)
+    return fail(FP8TS_EINVAL, "%s: negative stride", fn);
+  if (out) {
+    if (out_head_stride < head_dim && num_heads > 1)
+      return fail(FP8TS_EINVAL, "%s: out_head_stride %lld < head_dim %d", fn, (long long)out_head_stride, head_dim);
+    if (num_tokens > 1 && out_token_stride < (int64_t)(num_heads - 1) * out_head_stride + head_dim)
+      return fail(FP8TS_EINVAL, "%s: out_token_stride %lld overlaps rows", fn, (long long)out_token_stride);
+  }
+  const bool aligned =
+      (uintptr_t)x % 16 == 0 && x_token_stride % 8 == 0 && x_head_stride % 8 == 0 &&
+      (uintptr_t)norm_weight % 16 == 0 && (rope_dim == 0 || (uintptr_t)cos_sin_cache % 16 == 0) &&
+      (!out || ((uintptr_t)out % 8 == 0 && out_token_stride % 8 == 0 && out_head_stride % 8 == 0)) &&
+      (!slot_mapping || (uintptr_t)cache % 8 == 0);
+  if (!aligned)
+    return fail(FP8TS_EUNSUPPORTED, "%s: x, norm_weight and cos_sin_cache need 16-byte alignment, out and cache 8-byte, and every stride a multiple of 8", fn);
+  const size_t xb = (size_t)((num_tokens - 1) * x_token_stride + (int64_t)(num_heads - 1) * x_head_stride + head_dim) * 2;
+  const size_t cb = slot_mapping ? (size_t)(num_pages * page_size) * num_heads * head_dim : 0;
+  struct { const void *p; size_t n; const char *name; } ins[] = {
+      {x, xb, "x"}, {norm_weight, (size_t)head_dim * 4, "norm_weight"},
+      {cos_sin_cache, rope_dim > 0 ? (size_t)(max_position * rope_dim * 4) : 0, "cos_sin_cache"},
+      {positions, rope_dim > 0 ? (size_t)num_tokens * 8 : 0, "positions"},
+      {slot_mapping, slot_mapping ? (size_t)num_tokens * 8 : 0, "slot_mapping"}};
+  if (out) {
+    const size_t ob = (size_t)((num_tokens - 1) * out_token_stride + (int64_t)(num_heads - 1) * out_head_stride + head_dim);
+    for (const auto &in : ins)
+      if (overlaps(out, ob, in.p, in.n)) return fail(FP8TS_EINVAL, "%s: out overlaps %s", fn, in.name);
+    if (overlaps(out, ob, cache, cb)) return fail(FP8TS_EINVAL, "%s: out overlaps cache", fn);
+  }
+  if (slot_mapping)
+    for (const auto &in : ins)
+      if (overlaps(cache, cb, in.p, in.n)) return fail(FP8TS_EINVAL, "%s: cache overlaps %s", fn, in.name);
+  NormRopeArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.x_ts = x_token_stride;
+  a.x_hs = x_head_stride;
+  a.weight = norm_weight;
+  a.eps = eps;
+  a.cos_sin = cos_sin_cache;
+  a.positions = positions;
+  a.out = out;
+  a.out_ts = out_token_stride;
+  a.out_hs = out_head_stride;
+  a.slot_mapping = slot_mapping;
+  a.cache = cache;
+  a.num_slots = slot_mapping ? num_pages * page_size : 0;
+  a.page_size = slot_mapping ? page_size : 1;
+  a.num_tokens = num_tokens;
+  a.max_position = max_position;
+  a.heads = num_heads;
+  a.dim = head_dim;
+  a.rope = rope_dim;
+  a.neox = is_neox != 0;
+  const float inv = has ? 1.0f / sv : 1.0f;   // fp32 reciprocal, rounded once
+  return launch_qknorm_rope_quantize(a, x_dtype, has, inv, stream);
+}
+
 size_t indexer_topk_workspace_size(int32_t total_q, int32_t num_heads, int32_t max_blocks) {
   if (total_q <= 0 || num_heads <= 0 || max_blocks <= 0) return 0;
   return indexer_workspace_bytes(total_q, num_heads, max_blocks);

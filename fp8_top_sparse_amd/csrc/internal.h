@@ -47,6 +47,26 @@ struct RopeArgs {
 int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float scale_inv,
                          hipStream_t stream);
 
+struct NormRopeArgs {
+  const uint16_t *x;                 // row (n, h) at x + n * x_ts + h * x_hs, dim elements
+  int64_t x_ts, x_hs;
+  const float *weight;               // [dim]
+  float eps;
+  const float *cos_sin;              // [max_position, rope]: cosines then sines
+  const int64_t *positions;          // [N]
+  uint8_t *out;                      // NULL or row (n, h) at out + n * out_ts + h * out_hs
+  int64_t out_ts, out_hs;
+  const int64_t *slot_mapping;       // NULL or [N]
+  uint8_t *cache;                    // [num_pages, heads, page_size, dim]
+  int64_t num_slots;                 // num_pages * page_size
+  int32_t page_size;
+  int64_t num_tokens, max_position;
+  int32_t heads, dim, rope;
+  bool neox;
+};
+int launch_qknorm_rope_quantize(const NormRopeArgs &a, int dtype, bool has_scale, float scale_inv,
+                                hipStream_t stream);
+
 // ---- indexer
 struct IndexerArgs {
   const uint8_t *idx_q;

@@ -405,6 +405,108 @@ int launch_rope_typed(const RopeArgs &a, float s, hipStream_t stream) {
   return check_launch("fp8_rope_quantize");
 }
 
+// Per-head RMS norm + RoPE + e4m3 (+ paged store) of index q / k rows.
+// One wave per (token, head) row, 8 consecutive dims per lane (dim <= 512).
+// The squares are summed in fp64, where each is exact, so the normaliser does
+// not depend on the reduction order; r = fl32(1 / sqrt(ss / dim + eps)) in
+// fp64; y = fl32(fl32(x r) w); then the rope_quantize rotation and encode.
+// A rotate-half partner lives in another lane and comes by shuffle.
+template <int DT, bool HAS_SCALE, bool NEOX>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float s) {
+#pragma clang fp contract(off)
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.num_tokens * a.heads) return;            // whole wave
+  const int64_t n = row / a.heads;
+  const int h = (int)(row - n * a.heads);
+  const int j0 = 8 * lane;
+  const bool act = j0 < a.dim;
+  v4u w = {0u, 0u, 0u, 0u};
+  if (act) w = *reinterpret_cast<const v4u *>(a.x + n * a.x_ts + (int64_t)h * a.x_hs + j0);
+  float x[8];
+  widen8<DT>(w, x);
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += (double)x[e] * (double)x[e];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const double den = sqrt(ss / (double)a.dim + (double)a.eps);
+  const float r = (float)(1.0 / den);
+  float y[8];
+  if (act) {
+    const v4f w0 = *reinterpret_cast<const v4f *>(a.weight + j0);
+    const v4f w1 = *reinterpret_cast<const v4f *>(a.weight + j0 + 4);
+    const float wt[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (x[e] * r) * wt[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+  }
+  const int nope = a.dim - a.rope, half = a.rope / 2;
+  const bool rope = act && j0 >= nope;
+  const bool first = j0 - nope < half;
+  float p[8];
+  if constexpr (NEOX) {
+    // every lane takes part in the shuffles; only rope lanes use the result
+    const int src = rope ? (first ? lane + half / 8 : lane - half / 8) : lane;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __shfl(y[e], src);
+  }
+  if (!act) return;
+  v2u code;
+  if (!rope) {
+    code = encode8<HAS_SCALE>(y, s);
+  } else {
+    const int64_t pos = a.positions[n];
+    if (pos < 0 || pos >= a.max_position) {
+      code = (v2u){0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    } else {
+      const float *cs = a.cos_sin + pos * a.rope;
+      const int jr = j0 - nope;
+      float o[8];
+      if constexpr (NEOX) {
+        const int i0 = first ? jr : jr - half;
+        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0), cb = *reinterpret_cast<const v4f *>(cs + i0 + 4);
+        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0),
+                  sb = *reinterpret_cast<const v4f *>(cs + half + i0 + 4);
+        const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
+        const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+        rope8<true>(y, p, cv, sv, first, o);
+      } else {
+        const int i0 = jr / 2;
+        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0);
+        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0);
+        const float cv[4] = {ca[0], ca[1], ca[2], ca[3]}, sv[4] = {sa[0], sa[1], sa[2], sa[3]};
+        rope8<false>(y, nullptr, cv, sv, false, o);
+      }
+      code = encode8<HAS_SCALE>(o, s);
+    }
+  }
+  if (a.out) *reinterpret_cast<v2u *>(a.out + n * a.out_ts + (int64_t)h * a.out_hs + j0) = code;
+  if (a.slot_mapping) {
+    const int64_t slot = a.slot_mapping[n];
+    if (slot >= 0 && slot < a.num_slots) {
+      const int64_t pg = slot / a.page_size, off = slot - pg * a.page_size;
+      *reinterpret_cast<v2u *>(a.cache + ((pg * a.heads + h) * a.page_size + off) * a.dim + j0) = code;
+    }
+  }
+}
+
+template <int DT, bool HAS_SCALE>
+int launch_qknorm_typed(const NormRopeArgs &a, float s, hipStream_t stream) {
+  const int64_t blocks = (a.num_tokens * a.heads + 3) / 4;   // one wave per row
+  if (a.neox) {
+    hipLaunchKernelGGL((qknorm_rope_kernel<DT, HAS_SCALE, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a, s);
+  } else {
+    hipLaunchKernelGGL((qknorm_rope_kernel<DT, HAS_SCALE, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a, s);
+  }
+  return check_launch("fp8_qknorm_rope_quantize");
+}
+
 }  // namespace
 
 int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float scale_inv,
@@ -415,6 +517,16 @@ int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float sca
   }
   return has_scale ? launch_rope_typed<FP8TS_FP16, true>(a, scale_inv, stream)
                    : launch_rope_typed<FP8TS_FP16, false>(a, 1.0f, stream);
+}
+
+int launch_qknorm_rope_quantize(const NormRopeArgs &a, int dtype, bool has_scale, float scale_inv,
+                                hipStream_t stream) {
+  if (dtype == FP8TS_BF16) {
+    return has_scale ? launch_qknorm_typed<FP8TS_BF16, true>(a, scale_inv, stream)
+                     : launch_qknorm_typed<FP8TS_BF16, false>(a, 1.0f, stream);
+  }
+  return has_scale ? launch_qknorm_typed<FP8TS_FP16, true>(a, scale_inv, stream)
+                   : launch_qknorm_typed<FP8TS_FP16, false>(a, 1.0f, stream);
 }
 
 int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scale_inv,

@@ -21,6 +21,9 @@
  *                      of Q or K (no-rope part ++ rotated rope part per row).
  *   fp8_cache_store    quantize new K / V / index-K rows (or MLA latent + rope
  *                      rows) and scatter them into the paged e4m3 caches.
+ *   fp8_qknorm_rope_quantize  per-head RMS norm + RoPE + quantization of the
+ *                      index query / index key, writing fp8 rows and/or
+ *                      storing them into the paged index-K cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -194,6 +197,53 @@ int fp8_cache_store(const void *x, const void *x2, int32_t x_dtype, int64_t num_
                     int64_t x_head_stride, int64_t x2_token_stride, int64_t x2_head_stride,
                     const int64_t *slot_mapping, uint8_t *cache, int64_t num_pages,
                     int32_t page_size, const float *scale, hipStream_t stream);
+
+/*
+ * fp8_qknorm_rope_quantize - per-head RMS normalisation, RoPE and e4m3
+ * quantization of index queries or index keys, with an optional store of the
+ * codes into a paged cache:
+ *   y    = x * r * w,  r = 1 / sqrt(mean(x^2) + eps)   (over each head's head_dim values)
+ *   code = e4m3(nope(y) * inv) ++ e4m3(rope(last rope_dim dims of y, positions[n]) * inv)
+ * with inv = fl32(1 / scale) (None: no multiply).
+ *
+ * This is the fused qk-norm + RoPE + index-insert producer of the MiniMax
+ * sparse layer, which emits the index query directly in fp8 when the index
+ * cache is e4m3 (vLLM PR 45892 digest, implementation steps 3 and 5).  The
+ * pages give no formula for the norm; the one above is RMS normalisation with
+ * a learned per-dim weight.  Precision: the squares are summed in fp64 (each
+ * square of a bf16 / fp16 value is exact there, so the sum is independent of
+ * order unless a row's magnitudes span more than fp64 holds); then
+ * r = fl32(1 / sqrt(fl64(sum / head_dim) + eps)) in fp64, y = fl32(fl32(x r) w).
+ * RoPE, rounding, saturation and NaN as in fp8_rope_quantize (the no-rope
+ * dims come first in the row, the rotated dims last).
+ *
+ * x               device, dtype x_dtype; (n, h, c) at x[n * x_token_stride + h * x_head_stride + c].
+ * norm_weight     device fp32 [head_dim].   eps: host float >= 0.
+ * cos_sin_cache, positions, is_neox: as in fp8_rope_quantize (rope_dim wide);
+ *                 an invalid position writes 0x7F over the rope bytes.
+ * out             device e4m3 or NULL; row (n, h) of head_dim bytes at
+ *                 out + n * out_token_stride + h * out_head_stride.
+ * slot_mapping    device int64 [num_tokens] or NULL; with it, row (n, h) is
+ *                 also stored into cache [num_pages, num_heads, page_size,
+ *                 head_dim] at page s / page_size, offset s % page_size,
+ *                 s = slot_mapping[n]; negative or out-of-range slots store
+ *                 nothing (as fp8_cache_store).  At least one of out and
+ *                 slot_mapping must be given.
+ * head_dim a multiple of 8 and at most 512; rope_dim a multiple of 16 (0 for
+ * no rotation) and at most head_dim; x, norm_weight and cos_sin_cache 16-byte
+ * aligned, out and cache 8-byte aligned, every stride a multiple of 8
+ * (FP8TS_EUNSUPPORTED otherwise).  num_tokens == 0 is a no-op.
+ * Errors: FP8TS_EINVAL for null pointers, bad sizes, a negative or non-finite
+ * eps, a bad scale, overlapping output rows, or an output overlapping an input.
+ */
+int fp8_qknorm_rope_quantize(const void *x, int32_t x_dtype, int64_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t rope_dim, int64_t x_token_stride,
+                             int64_t x_head_stride, const float *norm_weight, float eps,
+                             const float *cos_sin_cache, int64_t max_position,
+                             const int64_t *positions, int32_t is_neox, uint8_t *out,
+                             int64_t out_token_stride, int64_t out_head_stride,
+                             const int64_t *slot_mapping, uint8_t *cache, int64_t num_pages,
+                             int32_t page_size, const float *scale, hipStream_t stream);
 
 /*
  * indexer_topk - ascending top-k block ids of the lightning indexer.

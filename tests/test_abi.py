@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
-              "fp8ts_last_error",
+              "fp8_qknorm_rope_quantize", "fp8ts_last_error",
               "indexer_topk_workspace_size", "sparse_attn_workspace_size", "fp8ts_abi_version"):
         assert n in names
 
@@ -142,6 +142,50 @@ def test_rope_quantize_validation(lib):
     assert rq(lib, out=ctypes.c_void_p(0x1000)) == EINVAL and "overlaps" in last(lib)
     assert rq(lib, n=1 << 22) == EUNSUP and "2^31" in last(lib)
     assert rq(lib, n=0, xp=None, out=None) == 0
+
+
+# ----------------------------------------------------------- fp8_qknorm_rope_quantize
+def qn(lib, **kw):
+    a = dict(x=FAKE, dt=0, n=8, h=4, d=128, rope=64, xts=512, xhs=128, w=ctypes.c_void_p(0x3000), eps=1e-6,
+             cs=ctypes.c_void_p(0x10000000), maxp=4096, pos=ctypes.c_void_p(0x20000000), neox=1,
+             out=ctypes.c_void_p(0x40000000), ots=512, ohs=128, slots=None, cache=None, pages=0, page=128,
+             scale=None)
+    a.update(kw)
+    return lib.fp8_qknorm_rope_quantize(a["x"], a["dt"], a["n"], a["h"], a["d"], a["rope"], a["xts"], a["xhs"],
+                                        a["w"], a["eps"], a["cs"], a["maxp"], a["pos"], a["neox"], a["out"],
+                                        a["ots"], a["ohs"], a["slots"], a["cache"], a["pages"], a["page"],
+                                        a["scale"], None)
+
+
+def test_qknorm_rope_quantize_validation(lib):
+    assert qn(lib, dt=2) == EINVAL and "x_dtype" in last(lib)
+    assert qn(lib, n=-1) == EINVAL
+    assert qn(lib, h=0) == EINVAL
+    assert qn(lib, rope=63) == EINVAL and "rope_dim" in last(lib)
+    assert qn(lib, rope=256) == EINVAL                                 # rope_dim > head_dim
+    assert qn(lib, eps=-1.0) == EINVAL and "eps" in last(lib)
+    assert qn(lib, eps=float("inf")) == EINVAL
+    assert qn(lib, out=None) == EINVAL and "neither" in last(lib)      # nothing to write
+    assert qn(lib, slots=FAKE2, cache=ctypes.c_void_p(0x50000000), pages=4, page=0) == EINVAL
+    assert qn(lib, d=100) == EUNSUP and "head_dim" in last(lib)
+    assert qn(lib, d=1024, rope=64, xts=4096, xhs=1024, ots=4096, ohs=1024) == EUNSUP
+    assert qn(lib, rope=24) == EUNSUP
+    assert qn(lib, scale=sc(0.0)) == EINVAL and "scale" in last(lib)
+    assert qn(lib, w=None) == EINVAL
+    assert qn(lib, pos=None) == EINVAL
+    assert qn(lib, slots=FAKE2) == EINVAL and "cache" in last(lib)     # slots without a cache
+    assert qn(lib, slots=FAKE2, cache=ctypes.c_void_p(0x50000000), pages=0) == EINVAL
+    assert qn(lib, maxp=0) == EINVAL
+    assert qn(lib, ohs=100) == EINVAL and "out_head_stride" in last(lib)
+    assert qn(lib, ots=128) == EINVAL and "out_token_stride" in last(lib)
+    assert qn(lib, x=ctypes.c_void_p(0x1008)) == EUNSUP and "alignment" in last(lib)
+    assert qn(lib, w=ctypes.c_void_p(0x3004)) == EUNSUP
+    assert qn(lib, out=ctypes.c_void_p(0x1000)) == EINVAL and "out overlaps x" in last(lib)
+    assert qn(lib, out=None, slots=FAKE2, cache=ctypes.c_void_p(0x3000), pages=4) == EINVAL and \
+        "cache overlaps norm_weight" in last(lib)
+    assert qn(lib, n=1 << 22) == EUNSUP and "2^31" in last(lib)
+    # rope_dim 0 needs no cos/sin or positions; an empty call launches nothing
+    assert qn(lib, n=0, x=None, w=None) == 0
 
 
 # ----------------------------------------------------------- indexer_topk
@@ -280,6 +324,9 @@ int main(void) {
   if (fp8_rope_quantize(NULL, (const void *)0x1000, FP8TS_BF16, 4, 1, 0, 63, 0, 0, 64, 64,
                         (const float *)0x2000, 16, (const int64_t *)0x3000, 1, (uint8_t *)0x100000, 64, 64, NULL, 0)
       != FP8TS_EINVAL) return 16;
+  if (fp8_qknorm_rope_quantize((const void *)0x1000, FP8TS_BF16, 4, 4, 128, 64, 512, 128, (const float *)0x2000,
+                               -1.0f, (const float *)0x3000, 16, (const int64_t *)0x4000, 1, (uint8_t *)0x100000,
+                               512, 128, NULL, NULL, 0, 128, NULL, 0) != FP8TS_EINVAL) return 19;
   if (sparse_attn_workspace_size(FP8TS_BLOCK_MODE, 0, 0, 0, 16, 2, 4, 128, 64, 8) != 0) return 17;
   /* empty inputs are no-ops */
   if (fp8_quantize(NULL, FP8TS_FP16, 0, 8, 8, NULL, 8, NULL, 0) != FP8TS_OK) return 18;
