@@ -219,6 +219,54 @@ def measure_rope_quantize(fts, Q, reps: int) -> dict:
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
+def measure_qknorm_rope_quantize(fts, T: int, hidx: int, reps: int) -> dict:
+    """fp8_qknorm_rope_quantize of a step's index rows: the index query
+    [T, hidx, 128] into fp8 rows and the T new index keys [T, 128] stored into
+    the paged index-K cache, both with the last 64 dims rotated (rotate-half,
+    RoFormer angles, positions 0..T-1), seeded N(0, 1) bf16 inputs.
+
+    Algorithmic bytes: 2 read + 1 written per element, plus per token its
+    position (8 B, read by both calls), slot (8 B) and the two fp32 cos/sin
+    rows (256 B each call).  The same 512 MiB read flush as the other producers
+    runs between repetitions.
+    """
+    import torch
+    R, D = 64, 128
+    g = torch.Generator(device="cuda").manual_seed(11)
+    iq = torch.randn((T, hidx, D), generator=g, device="cuda").to(torch.bfloat16)
+    ik = torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
+    w = torch.rand(D, generator=g, device="cuda") + 0.5
+    i = np.arange(R // 2, dtype=np.float64)
+    ang = np.arange(T, dtype=np.float64)[:, None] * 10000.0 ** (-2.0 * i / R)[None, :]
+    cache = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).cuda()
+    pos = torch.arange(T, dtype=torch.int64, device="cuda")
+    pages = (T + PAGE - 1) // PAGE
+    kc = torch.empty((pages, PAGE, D), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, hidx, D), dtype=torch.uint8, device="cuda")
+    nbytes = 3 * (iq.numel() + ik.numel()) + T * (8 + 8 + 8 + 2 * 4 * R)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+
+    def run():
+        fts.fp8_qknorm_rope_quantize(iq, w, 1e-6, rope_dim=R, cos_sin_cache=cache, positions=pos, out=out)
+        fts.fp8_qknorm_rope_quantize(ik, w, 1e-6, rope_dim=R, cos_sin_cache=cache, positions=pos,
+                                     write_out=False, slot_mapping=pos, cache=kc)
+
+    run()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.mean(times))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"launches": 2, "ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -407,6 +455,8 @@ def main():
                               "algorithmic_bytes": int(dbytes)}
 
     result["cache_store"] = measure_cache_store(fts, wl, block, args.steps)
+    if block:
+        result["qknorm_rope_quantize"] = measure_qknorm_rope_quantize(fts, int(T), int(Hidx), args.steps)
     if not block:
         result["rope_quantize"] = measure_rope_quantize(fts, Q, args.steps)
 

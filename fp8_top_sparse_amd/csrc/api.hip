@@ -291,6 +291,8 @@ int fp8_qknorm_rope_quantize(const void *x, int32_t x_dtype, int64_t num_tokens,
   a.heads = num_heads;
   a.dim = head_dim;
   a.rope = rope_dim;
+  a.lanes_per_row = 1;
+  while (a.lanes_per_row * 8 < head_dim) a.lanes_per_row *= 2;
   a.neox = is_neox != 0;
   const float inv = has ? 1.0f / sv : 1.0f;   // fp32 reciprocal, rounded once
   return launch_qknorm_rope_quantize(a, x_dtype, has, inv, stream);

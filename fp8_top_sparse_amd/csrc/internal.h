@@ -62,6 +62,7 @@ struct NormRopeArgs {
   int32_t page_size;
   int64_t num_tokens, max_position;
   int32_t heads, dim, rope;
+  int32_t lanes_per_row;             // dim / 8 rounded up to a power of two
   bool neox;
 };
 int launch_qknorm_rope_quantize(const NormRopeArgs &a, int dtype, bool has_scale, float scale_inv,

@@ -406,7 +406,10 @@ int launch_rope_typed(const RopeArgs &a, float s, hipStream_t stream) {
 }
 
 // Per-head RMS norm + RoPE + e4m3 (+ paged store) of index q / k rows.
-// One wave per (token, head) row, 8 consecutive dims per lane (dim <= 512).
+// One group of `lpr` lanes per (token, head) row, 8 consecutive dims per lane
+// (lpr = dim / 8 rounded up to a power of two, so a 128-dim row takes 16
+// lanes and a wave holds four rows; dim <= 512).  Reductions and partner
+// shuffles stay inside a group.
 // The squares are summed in fp64, where each is exact, so the normaliser does
 // not depend on the reduction order; r = fl32(1 / sqrt(ss / dim + eps)) in
 // fp64; y = fl32(fl32(x r) w); then the rope_quantize rotation and encode.
@@ -416,12 +419,17 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
 #pragma clang fp contract(off)
   typedef float v4f __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.num_tokens * a.heads) return;            // whole wave
-  const int64_t n = row / a.heads;
-  const int h = (int)(row - n * a.heads);
-  const int j0 = 8 * lane;
-  const bool act = j0 < a.dim;
+  const int lpr = a.lanes_per_row;
+  const int gl = lane & (lpr - 1);                       // lane within the row's group
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / lpr);   // the wave's first row
+  const int64_t rows = a.num_tokens * a.heads;
+  if (row0 >= rows) return;                              // whole wave
+  const int64_t row = row0 + lane / lpr;
+  const bool live = row < rows;
+  const int64_t n = live ? row / a.heads : 0;
+  const int h = live ? (int)(row - n * a.heads) : 0;
+  const int j0 = 8 * gl;
+  const bool act = live && j0 < a.dim;
   v4u w = {0u, 0u, 0u, 0u};
   if (act) w = *reinterpret_cast<const v4u *>(a.x + n * a.x_ts + (int64_t)h * a.x_hs + j0);
   float x[8];
@@ -430,7 +438,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += (double)x[e] * (double)x[e];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  for (int m = lpr >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
   const double den = sqrt(ss / (double)a.dim + (double)a.eps);
   const float r = (float)(1.0 / den);
   float y[8];
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
   float p[8];
   if constexpr (NEOX) {
     // every lane takes part in the shuffles; only rope lanes use the result
-    const int src = rope ? (first ? lane + half / 8 : lane - half / 8) : lane;
+    const int src = rope ? (first ? lane + half / 8 : lane - half / 8) : lane;   // same group
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = __shfl(y[e], src);
   }
@@ -496,7 +504,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
 
 template <int DT, bool HAS_SCALE>
 int launch_qknorm_typed(const NormRopeArgs &a, float s, hipStream_t stream) {
-  const int64_t blocks = (a.num_tokens * a.heads + 3) / 4;   // one wave per row
+  const int64_t per_block = 4 * (64 / a.lanes_per_row);     // rows per 256-thread block
+  const int64_t blocks = (a.num_tokens * a.heads + per_block - 1) / per_block;
   if (a.neox) {
     hipLaunchKernelGGL((qknorm_rope_kernel<DT, HAS_SCALE, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        a, s);
