@@ -132,3 +132,60 @@ def test_graph_replay_is_bitexact(gpu, n):
         for k in ("out", "ml", "lse"):
             g_out[k].zero_()
         torch.cuda.synchronize()
+
+
+def test_producers_graph_replay_is_bitexact(gpu):
+    """The producers captured together: K/V rows stored by slot, RoPE +
+    quantize of MLA queries, qk-norm + RoPE + quantize of index queries (rows)
+    and index keys (stored by slot).  Every replay equals the eager result."""
+    g = torch.Generator().manual_seed(21)
+    k_new = torch.randn(300, 2, 128, generator=g).to(torch.bfloat16).cuda()
+    slots = torch.from_numpy(np.random.default_rng(22).permutation(4 * 128)[:300].astype(np.int64)).cuda()
+    q = torch.randn(64, 16, 576, generator=g).to(torch.bfloat16).cuda()
+    iq = torch.randn(64, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    ik = torch.randn(64, 128, generator=g).to(torch.bfloat16).cuda()
+    nw = (torch.rand(128, generator=g) + 0.5).cuda()
+    ang = np.arange(256)[:, None] * 10000.0 ** (-np.arange(32) / 32.0)[None, :]
+    cs = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)).cuda()
+    pos = (torch.arange(64, dtype=torch.int64) * 3).cuda()
+    islots = (torch.arange(64, dtype=torch.int64) * 2).cuda()
+
+    def outs():
+        return dict(kc=torch.zeros((4, 2, 128, 128), dtype=torch.uint8, device="cuda"),
+                    q8=torch.empty((64, 16, 576), dtype=torch.uint8, device="cuda"),
+                    iq8=torch.empty((64, 4, 128), dtype=torch.uint8, device="cuda"),
+                    ikc=torch.zeros((1, 128, 128), dtype=torch.uint8, device="cuda"))
+
+    def step(o):
+        fts.fp8_cache_store(k_new, slots, o["kc"], scale=0.75)
+        fts.fp8_rope_quantize(q[..., 512:], cs, pos, x_nope=q[..., :512], out=o["q8"], scale=1.5)
+        fts.fp8_qknorm_rope_quantize(iq, nw, 1e-6, rope_dim=64, cos_sin_cache=cs, positions=pos, out=o["iq8"])
+        fts.fp8_qknorm_rope_quantize(ik, nw, 1e-6, rope_dim=64, cos_sin_cache=cs, positions=pos, write_out=False,
+                                     slot_mapping=islots, cache=o["ikc"])
+
+    eager = outs()
+    step(eager)
+    torch.cuda.synchronize()
+    ref = _results(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g_out = outs()
+    with torch.cuda.stream(side):
+        step(g_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in g_out.values():
+            o.zero_()                      # eager fill kernels, outside the graph
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same(ref, _results(g_out), f"producer replay {r}")
+        other = outs()
+        step(other)
+        torch.cuda.synchronize()
+        _same(ref, _results(other), f"eager producers after replay {r}")
