@@ -1,7 +1,7 @@
 """Benchmark of the FP8 top-k sparse attention hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input, inputs resident
-in HBM: fp8_quantize(Q), fp8_quantize(idx_q), indexer_topk, sparse_attn_fwd.
+in HBM: fp8_quantize of Q and idx_q (one fp8_quantize_pair launch), indexer_topk, sparse_attn_fwd.
 Default workload: 8192-token causal GQA block-sparse prefill (16 q / 2 kv
 heads, d 128, page 128, 4 index heads, top-64 blocks).
 
@@ -56,6 +56,10 @@ def calibrate_copy(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
 
+
+# Q and idx_q quantized by one fp8_quantize_pair launch (same bytes as two
+# fp8_quantize calls); FP8TS_BENCH_SINGLE_QUANTIZE=1 times the two calls instead
+PAIR_QUANTIZE = os.environ.get("FP8TS_BENCH_SINGLE_QUANTIZE", "0") != "1"
 
 TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md",
                    5: "profiles/attn_block_decode__gqa_decode_b64_s32768_top64.md"}
@@ -336,9 +340,12 @@ def main():
             if ev is not None:
                 ev[k][i].record()
         rec("quant", 0)
-        fts.fp8_quantize(Q, wl.q_scale, out=q8)
-        if block:
-            fts.fp8_quantize(IQ, wl.idx_q_scale, out=iq8)
+        if block and PAIR_QUANTIZE:
+            fts.fp8_quantize_pair(Q, wl.q_scale, IQ, wl.idx_q_scale, out0=q8, out1=iq8)
+        else:
+            fts.fp8_quantize(Q, wl.q_scale, out=q8)
+            if block:
+                fts.fp8_quantize(IQ, wl.idx_q_scale, out=iq8)
         rec("quant", 1)
         if block:
             rec("index", 0)

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "fp8ts_last_error": ([], ctypes.c_char_p),
     "fp8ts_abi_version": ([], ctypes.c_int),
     "fp8_quantize": ([_vp, _i32, _i64, _i64, _i64, _vp, _i64, _fp, _vp], ctypes.c_int),
+    "fp8_quantize_pair": ([_vp, _vp, _i64, _fp, _vp, _vp, _i64, _fp, _i32, _vp], ctypes.c_int),
     "indexer_topk_workspace_size": ([_i32, _i32, _i32], _sz),
     "indexer_topk": ([_vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                       _fp, _fp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -170,6 +171,33 @@ def fp8_quantize(x: torch.Tensor, scale: Optional[float] = None, out: Optional[t
         raise ValueError("out does not flatten like x")
     _check(lib.fp8_quantize(_ptr(x), dt, rows, cols, xs, _ptr(out), os_, _scale(scale), _stream(stream)))
     return out
+
+
+def fp8_quantize_pair(x0: torch.Tensor, scale0: Optional[float], x1: torch.Tensor, scale1: Optional[float], *,
+                      out0: Optional[torch.Tensor] = None, out1: Optional[torch.Tensor] = None,
+                      stream=None):
+    """``(fp8_quantize(x0, scale0), fp8_quantize(x1, scale1))`` in one launch.
+
+    Both tensors contiguous, of one dtype (bf16 or fp16), with element counts
+    that are multiples of 8.  Returns ``(out0, out1)``, shaped like the inputs.
+    """
+    lib = load()
+    if x0.dtype != x1.dtype or x0.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"x0 and x1 must share a bf16 or fp16 dtype, got {x0.dtype} and {x1.dtype}")
+    dt = BF16 if x0.dtype == torch.bfloat16 else FP16
+    if not x0.is_contiguous() or not x1.is_contiguous():
+        raise ValueError("x0 and x1 must be contiguous")
+    outs = []
+    for x, o in ((x0, out0), (x1, out1)):
+        if o is None:
+            o = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        ob = _bytes(o)
+        if tuple(ob.shape) != tuple(x.shape) or not ob.is_contiguous():
+            raise ValueError(f"out shape {tuple(ob.shape)} != x shape {tuple(x.shape)}, or not contiguous")
+        outs.append((o, ob))
+    _check(lib.fp8_quantize_pair(_ptr(x0), _ptr(outs[0][1]), x0.numel(), _scale(scale0), _ptr(x1),
+                                 _ptr(outs[1][1]), x1.numel(), _scale(scale1), dt, _stream(stream)))
+    return outs[0][0], outs[1][0]
 
 
 def indexer_topk(idx_q: torch.Tensor, idx_k: torch.Tensor, block_table: torch.Tensor,
@@ -455,6 +483,6 @@ def fp8_qknorm_rope_quantize(x: torch.Tensor, norm_weight: torch.Tensor, eps: fl
     return out if write_out else None
 
 
-__all__ = ["fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
+__all__ = ["fp8_quantize", "fp8_quantize_pair", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
            "fp8_qknorm_rope_quantize", "load", "flatten_to_2d", "EXPORTED",
            "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

@@ -72,6 +72,31 @@ int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int
   return launch_quantize(x, x_dtype, rows, cols, x_row_stride, out, out_row_stride, has, inv, stream);
 }
 
+int fp8_quantize_pair(const void *x0, uint8_t *out0, int64_t n0, const float *scale0, const void *x1,
+                      uint8_t *out1, int64_t n1, const float *scale1, int32_t x_dtype, hipStream_t stream) {
+  const char *fn = "fp8_quantize_pair";
+  if (x_dtype != FP8TS_BF16 && x_dtype != FP8TS_FP16)
+    return fail(FP8TS_EINVAL, "%s: x_dtype must be 0 (bf16) or 1 (fp16), got %d", fn, x_dtype);
+  if (n0 < 0 || n1 < 0) return fail(FP8TS_EINVAL, "%s: negative size", fn);
+  bool h0 = false, h1 = false;
+  float v0 = 1.0f, v1 = 1.0f;
+  if (int st = read_scale(fn, "scale0", scale0, &h0, &v0)) return st;
+  if (int st = read_scale(fn, "scale1", scale1, &h1, &v1)) return st;
+  if (n0 == 0 && n1 == 0) return FP8TS_OK;
+  if ((n0 > 0 && (!x0 || !out0)) || (n1 > 0 && (!x1 || !out1))) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
+  if (n0 % 8 || n1 % 8)
+    return fail(FP8TS_EUNSUPPORTED, "%s: element counts must be multiples of 8 (got %lld, %lld)", fn, (long long)n0,
+                (long long)n1);
+  if ((n0 > 0 && ((uintptr_t)x0 % 16 || (uintptr_t)out0 % 8)) || (n1 > 0 && ((uintptr_t)x1 % 16 || (uintptr_t)out1 % 8)))
+    return fail(FP8TS_EUNSUPPORTED, "%s: x needs 16-byte and out 8-byte alignment", fn);
+  const size_t xb0 = (size_t)n0 * 2, xb1 = (size_t)n1 * 2, ob0 = (size_t)n0, ob1 = (size_t)n1;
+  if (overlaps(out0, ob0, x0, xb0) || overlaps(out0, ob0, x1, xb1) || overlaps(out1, ob1, x0, xb0) ||
+      overlaps(out1, ob1, x1, xb1) || overlaps(out0, ob0, out1, ob1))
+    return fail(FP8TS_EINVAL, "%s: an output overlaps an input or the other output", fn);
+  const float i0 = h0 ? 1.0f / v0 : 1.0f, i1 = h1 ? 1.0f / v1 : 1.0f;   // fp32 reciprocals, rounded once
+  return launch_quantize_pair(x0, out0, n0, h0, i0, x1, out1, n1, h1, i1, x_dtype, stream);
+}
+
 int fp8_cache_store(const void *x, const void *x2, int32_t x_dtype, int64_t num_tokens,
                     int32_t num_heads, int32_t dim, int32_t dim2, int64_t x_token_stride,
                     int64_t x_head_stride, int64_t x2_token_stride, int64_t x2_head_stride,

@@ -16,6 +16,9 @@ int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int check_launch(const char *what);
 
 // ---- quantize
+// n0 and n1 multiples of 8; contiguous, x 16-byte and out 8-byte aligned
+int launch_quantize_pair(const void *x0, uint8_t *out0, int64_t n0, bool has0, float inv0, const void *x1,
+                         uint8_t *out1, int64_t n1, bool has1, float inv1, int dtype, hipStream_t stream);
 int launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_stride,
                     uint8_t *out, int64_t out_stride, bool has_scale, float scale_inv,
                     hipStream_t stream);

@@ -96,6 +96,65 @@ __global__ __launch_bounds__(256) void quantize_flat_kernel(const uint16_t *__re
   if (t < 8 && e < n) out[e] = quant1<DT, HAS_SCALE>(x[e], s);
 }
 
+// Two contiguous tensors of one dtype, each with its own scale, in one launch:
+// chunk i < c0 belongs to the first, the rest to the second (a wave straddles
+// the boundary at most once).  Same codes as two quantize_flat_kernel launches.
+template <int DT, bool H0, bool H1>
+__global__ __launch_bounds__(256) void quantize_pair_kernel(const uint16_t *__restrict__ x0,
+                                                             uint8_t *__restrict__ o0, int64_t c0, float s0,
+                                                             const uint16_t *__restrict__ x1,
+                                                             uint8_t *__restrict__ o1, int64_t c1, float s1) {
+  const v4u *xv0 = reinterpret_cast<const v4u *>(x0);
+  const v4u *xv1 = reinterpret_cast<const v4u *>(x1);
+  v2u *ov0 = reinterpret_cast<v2u *>(o0);
+  v2u *ov1 = reinterpret_cast<v2u *>(o1);
+  const int64_t total = c0 + c1;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += 2 * stride) {
+    // two independent 16-byte loads in flight per thread
+    const int64_t j = i + stride;
+    const bool has_j = j < total;
+    const v4u a = __builtin_nontemporal_load(i < c0 ? xv0 + i : xv1 + (i - c0));
+    v4u b = {0u, 0u, 0u, 0u};
+    if (has_j) b = __builtin_nontemporal_load(j < c0 ? xv0 + j : xv1 + (j - c0));
+    if (i < c0) {
+      __builtin_nontemporal_store(quant8<DT, H0>(a, s0), ov0 + i);
+    } else {
+      __builtin_nontemporal_store(quant8<DT, H1>(a, s1), ov1 + (i - c0));
+    }
+    if (has_j) {
+      if (j < c0) {
+        __builtin_nontemporal_store(quant8<DT, H0>(b, s0), ov0 + j);
+      } else {
+        __builtin_nontemporal_store(quant8<DT, H1>(b, s1), ov1 + (j - c0));
+      }
+    }
+  }
+}
+
+template <int DT, bool H0, bool H1>
+int launch_pair_typed(const uint16_t *x0, uint8_t *o0, int64_t c0, float s0, const uint16_t *x1, uint8_t *o1,
+                      int64_t c1, float s1, hipStream_t stream) {
+  int64_t blocks = (c0 + c1 + 255) / 256;
+  blocks = blocks > 2048 ? (blocks + 1) / 2 : blocks;   // as the single-tensor launch
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((quantize_pair_kernel<DT, H0, H1>), dim3((unsigned)blocks), dim3(256), 0, stream, x0, o0, c0,
+                     s0, x1, o1, c1, s1);
+  return check_launch("fp8_quantize_pair");
+}
+
+template <int DT>
+int launch_pair_dt(const uint16_t *x0, uint8_t *o0, int64_t c0, bool h0, float s0, const uint16_t *x1,
+                   uint8_t *o1, int64_t c1, bool h1, float s1, hipStream_t stream) {
+  if (h0) {
+    return h1 ? launch_pair_typed<DT, true, true>(x0, o0, c0, s0, x1, o1, c1, s1, stream)
+              : launch_pair_typed<DT, true, false>(x0, o0, c0, s0, x1, o1, c1, s1, stream);
+  }
+  return h1 ? launch_pair_typed<DT, false, true>(x0, o0, c0, s0, x1, o1, c1, s1, stream)
+            : launch_pair_typed<DT, false, false>(x0, o0, c0, s0, x1, o1, c1, s1, stream);
+}
+
 // Row-strided 2-D view.  VEC: cols, both strides and both base pointers allow
 // 8-element vectors.  grid.x walks column chunks, grid.y walks rows.
 template <int DT, bool HAS_SCALE, bool VEC>
@@ -546,6 +605,14 @@ int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scal
   }
   return has_scale ? launch_store_typed<FP8TS_FP16, true>(a, scale_inv, stream)
                    : launch_store_typed<FP8TS_FP16, false>(a, 1.0f, stream);
+}
+
+int launch_quantize_pair(const void *x0, uint8_t *out0, int64_t n0, bool has0, float inv0, const void *x1,
+                         uint8_t *out1, int64_t n1, bool has1, float inv1, int dtype, hipStream_t stream) {
+  const uint16_t *a = static_cast<const uint16_t *>(x0), *b = static_cast<const uint16_t *>(x1);
+  if (dtype == FP8TS_BF16)
+    return launch_pair_dt<FP8TS_BF16>(a, out0, n0 / 8, has0, inv0, b, out1, n1 / 8, has1, inv1, stream);
+  return launch_pair_dt<FP8TS_FP16>(a, out0, n0 / 8, has0, inv0, b, out1, n1 / 8, has1, inv1, stream);
 }
 
 int launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t x_stride,

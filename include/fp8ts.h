@@ -5,7 +5,8 @@
  * Three operations, in the order a sparse-attention layer calls them:
  *
  *   fp8_quantize     per-tensor e4m3 quantization of the queries and the index
- *                    query (stored value = x / scale, None = unit scale).
+ *                    query (stored value = x / scale, None = unit scale);
+ *                    fp8_quantize_pair does both tensors in one launch.
  *   indexer_topk     lightning indexer: scores every 128-token KV block by the
  *                    maximum index logit over its visible tokens and writes the
  *                    top-k block ids of every (index head, query) in strictly
@@ -109,6 +110,25 @@ int fp8ts_abi_version(void);
 int fp8_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
                  int64_t x_row_stride, uint8_t *out, int64_t out_row_stride,
                  const float *scale, hipStream_t stream);
+
+/*
+ * fp8_quantize_pair - fp8_quantize of two contiguous tensors of one dtype,
+ * each with its own scale, in one launch: the queries and the index query of
+ * a sparse-attention layer, which the layer quantizes per tensor with their
+ * own scales (sglang PR 30971 digest, implementation step 3) right before the
+ * indexer and the attention.  Codes are those of two fp8_quantize calls.
+ *
+ * x0, x1          device, n0 / n1 elements of dtype x_dtype, contiguous,
+ *                 16-byte aligned.
+ * out0, out1      device e4m3, n0 / n1 bytes, contiguous, 8-byte aligned.
+ * scale0, scale1  host, NULL (None) or one finite float > 0 each.
+ * n0, n1          multiples of 8 (FP8TS_EUNSUPPORTED otherwise, as is a
+ *                 misaligned pointer: use fp8_quantize); either may be 0.
+ * Errors: FP8TS_EINVAL for null pointers, negative sizes, an unknown dtype, a
+ * bad scale, or any output overlapping an input or the other output.
+ */
+int fp8_quantize_pair(const void *x0, uint8_t *out0, int64_t n0, const float *scale0, const void *x1,
+                      uint8_t *out1, int64_t n1, const float *scale1, int32_t x_dtype, hipStream_t stream);
 
 /*
  * fp8_rope_quantize - rotary position embedding fused with e4m3 quantization,

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("fp8_quantize", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
+    for n in ("fp8_quantize", "fp8_quantize_pair", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
               "fp8_qknorm_rope_quantize", "fp8ts_last_error",
               "indexer_topk_workspace_size", "sparse_attn_workspace_size", "fp8ts_abi_version"):
         assert n in names
@@ -93,6 +93,28 @@ def cs(lib, **kw):
     return lib.fp8_cache_store(a["x"], a["x2"], a["dt"], a["n"], a["h"], a["d"], a["d2"], a["xts"], a["xhs"],
                                a["x2ts"], a["x2hs"], a["slots"], a["cache"], a["pages"], a["page"], a["scale"],
                                None)
+
+
+def qp(lib, **kw):
+    a = dict(x0=FAKE, o0=ctypes.c_void_p(0x10000000), n0=1024, s0=None, x1=ctypes.c_void_p(0x20000000),
+             o1=ctypes.c_void_p(0x30000000), n1=512, s1=None, dt=0)
+    a.update(kw)
+    return lib.fp8_quantize_pair(a["x0"], a["o0"], a["n0"], a["s0"], a["x1"], a["o1"], a["n1"], a["s1"], a["dt"],
+                                 None)
+
+
+def test_quantize_pair_validation(lib):
+    assert qp(lib, dt=4) == EINVAL and "x_dtype" in last(lib)
+    assert qp(lib, n1=-8) == EINVAL
+    assert qp(lib, s0=sc(0.0)) == EINVAL and "scale0" in last(lib)
+    assert qp(lib, s1=sc(float("inf"))) == EINVAL and "scale1" in last(lib)
+    assert qp(lib, x1=None) == EINVAL and "null" in last(lib)
+    assert qp(lib, n0=1004) == EUNSUP and "multiples of 8" in last(lib)
+    assert qp(lib, x0=ctypes.c_void_p(0x1008)) == EUNSUP and "alignment" in last(lib)
+    assert qp(lib, o1=ctypes.c_void_p(0x10000100)) == EINVAL and "overlaps" in last(lib)   # out1 inside out0
+    assert qp(lib, o0=ctypes.c_void_p(0x1100)) == EINVAL                                   # out0 inside x0
+    assert qp(lib, n0=0, n1=0, x0=None, x1=None, o0=None, o1=None) == 0
+    assert qp(lib, n0=0, x0=None, o0=None, s1=sc(-1.0)) == EINVAL                          # scales checked first
 
 
 def test_cache_store_validation(lib):

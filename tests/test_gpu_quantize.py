@@ -79,3 +79,48 @@ def test_mla_tiny_queries(gpu):
     wl = workload(1)
     got = host(gpu.fp8_quantize(bf16_dev(wl.q_bf16), wl.q_scale))
     assert np.array_equal(got, OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale))
+
+
+# ---------------------------------------------------------------- fp8_quantize_pair
+@pytest.mark.parametrize("dtype", [OQ.BF16, OQ.FP16])
+@pytest.mark.parametrize("s0,s1", [(None, None), (0.37, None), (None, 2.0), (0.25, 3.3)])
+def test_pair_every_bit_pattern(gpu, dtype, s0, s1):
+    """All 65536 patterns as the first tensor, a random second tensor of a
+    different size: both bit-exact against the oracle, each with its own scale."""
+    bits, x0 = all_patterns(dtype)
+    rng = np.random.default_rng(9)
+    f = rng.standard_normal(8 * 1237).astype(np.float32) * 50
+    b1 = W.bf16_bits(f) if dtype == OQ.BF16 else f.astype(np.float16).view(np.uint16)
+    x1 = torch.from_numpy(b1.view(np.int16)).view(x0.dtype).cuda()
+    g0, g1 = gpu.fp8_quantize_pair(x0.reshape(256, 256), s0, x1, s1)
+    assert np.array_equal(host(g0).reshape(-1), OQ.quantize(bits, dtype, s0))
+    assert np.array_equal(host(g1), OQ.quantize(b1, dtype, s1))
+
+
+@pytest.mark.parametrize("n", [2, 5])
+def test_pair_equals_two_single_calls_on_workload_queries(gpu, n):
+    """Q and idx_q of the 8k prefill and the decode workload: the pair launch
+    writes the bytes of two fp8_quantize calls, and the oracle's."""
+    wl = workload(n)
+    q, iq = bf16_dev(wl.q_bf16), bf16_dev(wl.idx_q_bf16)
+    g0, g1 = gpu.fp8_quantize_pair(q, wl.q_scale, iq, wl.idx_q_scale)
+    assert torch.equal(g0, gpu.fp8_quantize(q, wl.q_scale))
+    assert torch.equal(g1, gpu.fp8_quantize(iq, wl.idx_q_scale))
+    assert np.array_equal(host(g0), OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale))
+    assert np.array_equal(host(g1), OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale))
+
+
+def test_pair_edge_sizes(gpu):
+    """An empty tensor on either side, a single chunk, and tensors smaller than
+    one wave; bytes around the outputs untouched."""
+    rng = np.random.default_rng(10)
+    for n0, n1 in ((0, 64), (8, 0), (8, 8), (24, 4096), (4096 * 8 + 8, 16)):
+        b0 = W.bf16_bits(rng.standard_normal(n0).astype(np.float32))
+        b1 = W.bf16_bits(rng.standard_normal(n1).astype(np.float32))
+        buf = torch.full((n0 + n1 + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+        o0, o1 = buf[16:16 + n0], buf[32 + n0:32 + n0 + n1]
+        gpu.fp8_quantize_pair(bf16_dev(b0), 1.25, bf16_dev(b1), None, out0=o0, out1=o1)
+        assert np.array_equal(host(o0), OQ.quantize(b0, OQ.BF16, 1.25))
+        assert np.array_equal(host(o1), OQ.quantize(b1, OQ.BF16, None))
+        h = host(buf)
+        assert np.all(h[:16] == 0x5A) and np.all(h[16 + n0:32 + n0] == 0x5A) and np.all(h[32 + n0 + n1:] == 0x5A)
