@@ -491,6 +491,28 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
   const bool act = live && j0 < a.dim;
   v4u w = {0u, 0u, 0u, 0u};
   if (act) w = *reinterpret_cast<const v4u *>(a.x + n * a.x_ts + (int64_t)h * a.x_hs + j0);
+  // the position and its cos/sin rows do not depend on x: load them now, so
+  // their two dependent round trips overlap the row's load and reduction
+  const int nope = a.dim - a.rope, half = a.rope / 2;
+  const bool rope = act && j0 >= nope;
+  const bool first = j0 - nope < half;
+  const int jr = j0 - nope;
+  const int i0 = NEOX ? (first ? jr : jr - half) : jr / 2;
+  bool pos_ok = false;
+  v4f ca = {0.f, 0.f, 0.f, 0.f}, cb = ca, sa = ca, sb = ca;
+  if (rope) {
+    const int64_t pos = a.positions[n];
+    pos_ok = pos >= 0 && pos < a.max_position;
+    if (pos_ok) {
+      const float *cs = a.cos_sin + pos * a.rope;
+      ca = *reinterpret_cast<const v4f *>(cs + i0);
+      sa = *reinterpret_cast<const v4f *>(cs + half + i0);
+      if (NEOX) {
+        cb = *reinterpret_cast<const v4f *>(cs + i0 + 4);
+        sb = *reinterpret_cast<const v4f *>(cs + half + i0 + 4);
+      }
+    }
+  }
   float x[8];
   widen8<DT>(w, x);
   double ss = 0.0;
@@ -511,9 +533,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = 0.f;
   }
-  const int nope = a.dim - a.rope, half = a.rope / 2;
-  const bool rope = act && j0 >= nope;
-  const bool first = j0 - nope < half;
   float p[8];
   if constexpr (NEOX) {
     // every lane takes part in the shuffles; only rope lanes use the result
@@ -525,31 +544,19 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(NormRopeArgs a, float 
   v2u code;
   if (!rope) {
     code = encode8<HAS_SCALE>(y, s);
+  } else if (!pos_ok) {
+    code = (v2u){0x7F7F7F7Fu, 0x7F7F7F7Fu};
   } else {
-    const int64_t pos = a.positions[n];
-    if (pos < 0 || pos >= a.max_position) {
-      code = (v2u){0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    float o[8];
+    if constexpr (NEOX) {
+      const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
+      const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      rope8<true>(y, p, cv, sv, first, o);
     } else {
-      const float *cs = a.cos_sin + pos * a.rope;
-      const int jr = j0 - nope;
-      float o[8];
-      if constexpr (NEOX) {
-        const int i0 = first ? jr : jr - half;
-        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0), cb = *reinterpret_cast<const v4f *>(cs + i0 + 4);
-        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0),
-                  sb = *reinterpret_cast<const v4f *>(cs + half + i0 + 4);
-        const float cv[8] = {ca[0], ca[1], ca[2], ca[3], cb[0], cb[1], cb[2], cb[3]};
-        const float sv[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-        rope8<true>(y, p, cv, sv, first, o);
-      } else {
-        const int i0 = jr / 2;
-        const v4f ca = *reinterpret_cast<const v4f *>(cs + i0);
-        const v4f sa = *reinterpret_cast<const v4f *>(cs + half + i0);
-        const float cv[4] = {ca[0], ca[1], ca[2], ca[3]}, sv[4] = {sa[0], sa[1], sa[2], sa[3]};
-        rope8<false>(y, nullptr, cv, sv, false, o);
-      }
-      code = encode8<HAS_SCALE>(o, s);
+      const float cv[4] = {ca[0], ca[1], ca[2], ca[3]}, sv[4] = {sa[0], sa[1], sa[2], sa[3]};
+      rope8<false>(y, nullptr, cv, sv, false, o);
     }
+    code = encode8<HAS_SCALE>(o, s);
   }
   if (a.out) *reinterpret_cast<v2u *>(a.out + n * a.out_ts + (int64_t)h * a.out_hs + j0) = code;
   if (a.slot_mapping) {
