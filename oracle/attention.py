@@ -32,7 +32,8 @@ Readings taken where the pages are silent: ``lse`` includes the sink and is a
 natural log; ``max_logits`` is the maximum over key logits only.  Query head h
 uses index head ``h // (Hq / Hidx)`` and KV head ``h // (Hq / Hkv)``.  In block
 mode the key set is the union, over the row's ids ``0 <= b < max_blocks``, of
-tokens ``128 b .. 128 b + 127`` that are ``<= p``.  In token mode each valid
+tokens ``128 b .. 128 b + 127`` that are ``<= p``; a block whose block-table
+entry lies outside ``[0, num_pages)`` names no page and adds no key.  In token mode each valid
 list entry (``0 <= idx < S``, within ``topk_length``) contributes one term.
 
 Pins (tests/test_oracle_attention.py): closed forms (identical keys give
@@ -163,6 +164,7 @@ def sparse_attn_block(q8, k_cache8, v_cache8, ids, block_table, cu_seqlens_q, se
         for g in range(Hidx):
             blocks = np.unique(ids[g, t])
             blocks = blocks[(blocks >= 0) & (blocks < max_blocks)]
+            blocks = blocks[(bt[b, blocks] >= 0) & (bt[b, blocks] < kc.shape[0])]   # no page: no keys
             heads = np.arange(g * gq_idx, (g + 1) * gq_idx)
             for kvh in np.unique(heads // gq_kv):
                 hs = heads[heads // gq_kv == kvh]

@@ -26,6 +26,11 @@ Readings taken where the pages are silent
   with ``sigma = sm_scale * idx_q_scale * idx_k_scale`` (each scale ``None``
   means 1).  Plain maximum: no ReLU, no sum, no cross-head weighting.
 * Ties: larger score first, then the lower block id.  No forced blocks.
+* A block-table entry outside ``[0, num_pages)`` names no page: that block
+  holds no key, so its score is the maximum over an empty set, ``-inf``.  It
+  still counts among the ``nb`` visible blocks and stays a candidate, ranked
+  below every block that has a key (ties among such blocks go to the lower
+  id, as any tie does).
 
 Everything is float64 on dequantized e4m3 inputs; selection is a brute-force
 sort.
@@ -83,7 +88,8 @@ def block_scores(idx_q8, idx_k8, block_table, cu_seqlens_q, seq_lens, *, sm_scal
         pmax = int(pos[toks[sel]].max())
         nb_max = pmax // page_size + 1
         pages = bt[b, :nb_max]
-        keys = table[kc[pages]]                      # [nb_max, page, D]
+        has_page = (pages >= 0) & (pages < kc.shape[0])
+        keys = table[kc[np.where(has_page, pages, 0)]]   # [nb_max, page, D]; rows of absent pages are masked
         key_pos = np.arange(nb_max * page_size).reshape(nb_max, page_size)
         for c0 in range(0, len(sel), chunk):
             ids = sel[c0:c0 + chunk]
@@ -91,6 +97,7 @@ def block_scores(idx_q8, idx_k8, block_table, cu_seqlens_q, seq_lens, *, sm_scal
             qv = table[q[tt]]                        # [n, H, D]
             dots = np.einsum("nhd,bpd->nhbp", qv, keys, optimize=True) * sigma
             vis = key_pos[None, :, :] <= pos[tt][:, None, None]     # [n, nb_max, page]
+            vis = vis & has_page[None, :, None]                     # a block without a page has no key
             dots = np.where(vis[:, None, :, :], dots, -np.inf)
             s = dots.max(axis=3)                     # [n, H, nb_max]
             for r, i in enumerate(ids):

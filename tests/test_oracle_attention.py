@@ -288,3 +288,29 @@ def test_block_mode_head_mapping():
         assert np.allclose(out[0, h], ref[0][0, 0], atol=1e-13)
     for h in (2, 3, 4, 5):         # their index heads selected nothing
         assert np.all(out[0, h] == 0)
+
+
+def test_block_mode_out_of_range_page_adds_no_keys():
+    # ids {0, 1, 2} where block 1's table entry names no page (-1, then one past
+    # the cache): the keys are those of blocks 0 and 2 only, as in token mode
+    q, kc, vc, bt, cu, sl = _block_case(seq_len=400, Hq=4, Hkv=1, Hidx=1, seed=6)
+    T = q.shape[0]
+    t = 390
+    ids = np.full((1, T, 3), -1, np.int32)
+    ids[0, t] = [0, 1, 2]
+    keys = [j for j in range(t + 1) if j // PAGE in (0, 2)]
+    kv_rows = np.stack([kc[bt[0, j // PAGE], 0, j % PAGE] for j in keys])
+    v_rows = np.stack([vc[bt[0, j // PAGE], 0, j % PAGE] for j in keys])
+    ref = A.sparse_attn_token(q[t:t + 1], kv_rows, np.arange(len(keys))[None], sm_scale=0.3,
+                              d_v=v_rows.shape[1], v8=v_rows)
+    for bad in (-1, kc.shape[0]):
+        bt2 = bt.copy()
+        bt2[0, 1] = bad
+        out, lse, mx = A.sparse_attn_block(q, kc, vc, ids, bt2, cu, sl, sm_scale=0.3, tokens=[t])
+        assert np.allclose(out, ref[0], atol=1e-13) and np.allclose(lse, ref[1], atol=1e-13)
+        assert np.allclose(mx, ref[2], atol=1e-13)
+    # every selected block without a page: no keys at all
+    bt3 = bt.copy()
+    bt3[0, :3] = -1
+    out, lse, mx = A.sparse_attn_block(q, kc, vc, ids, bt3, cu, sl, sm_scale=0.3, tokens=[t])
+    assert np.all(out == 0) and np.all(np.isneginf(lse)) and np.all(np.isneginf(mx))

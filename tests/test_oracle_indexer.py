@@ -36,16 +36,18 @@ def brute_row(q8, k8, bt, cu, sl, t, h, sigma, topk):
     b = int(np.searchsorted(cu, t, side="right") - 1)
     q_len = int(cu[b + 1] - cu[b])
     p = int(sl[b]) - q_len + (t - int(cu[b]))
-    best = {}
+    nb = p // PAGE + 1
+    best = {blk: -np.inf for blk in range(nb)}    # a block whose page is missing keeps -inf
     for j in range(p + 1):
         page = int(bt[b, j // PAGE])
+        if page < 0 or page >= k8.shape[0]:
+            continue                                # no page: the block holds no key
         dot = 0.0
         for d in range(q8.shape[2]):
             dot += tab[q8[t, h, d]] * tab[k8[page, j % PAGE, d]]
         s = sigma * dot
         blk = j // PAGE
-        best[blk] = max(best.get(blk, -np.inf), s)
-    nb = p // PAGE + 1
+        best[blk] = max(best[blk], s)
     if nb <= topk:
         return list(range(nb)) + [-1] * (topk - nb)
     items = sorted(best.items(), key=lambda kv: (-kv[1], kv[0]))[:topk]
@@ -140,3 +142,26 @@ def test_varlen_positions_and_decode():
     seq, pos = IX.positions(cu, sl)
     assert list(seq) == [0, 0, 0, 1]
     assert list(pos) == [7, 8, 9, 299]
+
+
+def test_out_of_range_pages_hold_no_keys():
+    """A block-table entry outside [0, num_pages) names no page: its block has
+    no key and scores -inf, below every block with a key, but stays a
+    candidate (lowest ids first among such blocks)."""
+    q8, k8, bt, cu, sl = tiny_case(seq_len=1280, D=8, seed=5)
+    P = k8.shape[0]
+    bt = bt.copy()
+    bt[0, [2, 5, 7]] = [-1, P, P + 40]              # three blocks without a page
+    sc = IX.block_scores(q8, k8, bt, cu, sl, sm_scale=0.25, tokens=[1279])[0]
+    assert np.all(np.isneginf(sc[:, [2, 5, 7]])) and np.all(np.isfinite(np.delete(sc, [2, 5, 7], axis=1)))
+    # 10 visible blocks, 7 with keys: top-4 picks among the 7 only
+    ids = IX.indexer_topk(q8, k8, bt, cu, sl, sm_scale=0.25, topk=4)
+    for t in (700, 1000, 1279):
+        for h in range(2):
+            row = list(ids[h, t])
+            assert not set(row) & {2, 5, 7}
+            assert row == brute_row(q8, k8, bt, cu, sl, t, h, 0.25, 4), (t, h)
+    # top-8 of the 10: all 7 blocks with keys, then the lowest id without one
+    ids8 = IX.indexer_topk(q8, k8, bt, cu, sl, sm_scale=0.25, topk=8)
+    assert list(ids8[0, 1279]) == [0, 1, 2, 3, 4, 6, 8, 9]
+    assert list(ids8[1, 1279]) == brute_row(q8, k8, bt, cu, sl, 1279, 1, 0.25, 8)
