@@ -1,18 +1,23 @@
 """Benchmark of the FP8 top-k sparse attention hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input, inputs resident
-in HBM: fp8_quantize of Q and idx_q (one fp8_quantize_pair launch), indexer_topk, sparse_attn_fwd.
-Default workload: 8192-token causal GQA block-sparse prefill (16 q / 2 kv
-heads, d 128, page 128, 4 index heads, top-64 blocks).
+in HBM: fp8_quantize of Q and idx_q (one fp8_quantize_pair launch),
+indexer_topk, sparse_attn_fwd.  Default workload: the 32768-token causal GQA
+block-sparse prefill with U(0.1, 4) per-tensor scales (16 q / 2 kv heads, d
+128, page 128, 4 index heads, top-64 of 256 blocks), where all three steps do
+real work.  The long-MLA prefill (4096 x 128 heads, top-2048 of 65536 tokens)
+and the decode batch (64 x 32k, top-64 blocks) follow under "extra_workloads"
+(--workload N times one of them alone).
 
 Prints ONE JSON line.  ``value`` = algorithmic attention TFLOP/s over the whole
 step, timed over K replays of the step captured as one HIP graph; ``roofline``
 describes the dominant kernel (sparse attention), timed with HIP events on the
-stream it runs on over K eager steps; ``cpu_baseline`` times the CPU oracle on a
+stream it runs on over K eager steps, each after a 512 MiB write that evicts
+the 256 MB last-level cache; ``cpu_baseline`` times the CPU oracle on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-       [--no-cpu-baseline]
+       [--no-extra] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -38,7 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads (4 and 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
@@ -62,11 +68,15 @@ def calibrate_copy(mib: int) -> None:
 PAIR_QUANTIZE = os.environ.get("FP8TS_BENCH_SINGLE_QUANTIZE", "0") != "1"
 
 TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md",
+                   3: "profiles/attn_block_prefill__gqa_prefill_32768_h16kv2_top64_scaled.md",
+                   4: "profiles/attn_token_mla__mla_prefill_4096x128_s65536_top2048.md",
                    5: "profiles/attn_block_decode__gqa_decode_b64_s32768_top64.md"}
 
 
 # the source file of the attention kernel that dominates each workload's step
 KERNEL_SOURCE = {2: "fp8_top_sparse_amd/csrc/attention_block.hip",
+                 3: "fp8_top_sparse_amd/csrc/attention_block.hip",
+                 4: "fp8_top_sparse_amd/csrc/attention_token.hip",
                  5: "fp8_top_sparse_amd/csrc/attention_decode.hip"}
 
 
@@ -271,24 +281,16 @@ def measure_qknorm_rope_quantize(fts, T: int, hidx: int, reps: int) -> dict:
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path", file=sys.stderr)
-        sys.exit(2)
-
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-
+def run_workload(n: int, steps: int, warmup: int, producers: bool) -> dict:
+    """Times workload n: K graph replays of the whole step (``value``), then K
+    eager steps with HIP events around each call (per-kernel times), each
+    eager step after a 512 MiB write that evicts the last-level cache."""
     import torch
     import fp8_top_sparse_amd as fts
     import workloads as W
 
-    fts.load()
-    torch.cuda.set_device(0)
-    wl = W.workload(args.workload)
+    lib = fts.load()
+    wl = W.workload(n)
 
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -311,7 +313,6 @@ def main():
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
         ml = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
         lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
-        lib = fts.load()
         iws = torch.empty(max(1, lib.indexer_topk_workspace_size(T, Hidx, wl.block_table.shape[1])),
                           dtype=torch.uint8, device="cuda")
         aws_n = lib.sparse_attn_workspace_size(1, wl.block_table.shape[0], T, wl.max_q_len, Hq, Hkv, Hidx, D,
@@ -326,7 +327,6 @@ def main():
         out = torch.empty((T, Hq, wl.d_v), dtype=torch.bfloat16, device="cuda")
         ml = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
         lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
-        lib = fts.load()
         aws_n = lib.sparse_attn_workspace_size(0, 0, T, 0, Hq, 1, 1, wl.d_v, wl.indices.shape[1], 0)
         aws = torch.empty(max(1, aws_n), dtype=torch.uint8, device="cuda")
 
@@ -366,22 +366,27 @@ def main():
                                 out=out, max_logits=ml, lse=lse, workspace=aws)
             rec("attn", 1)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # algorithmic work, counted from the path's own selections
+    index_flops = 0
+    index_scored = False
     if block:
         _, pos = token_positions(wl.cu_seqlens_q, wl.seq_lens)
         ids_h = ids.cpu().numpy()
         flops = block_attention_flops(ids_h, pos, Hq, Hidx, D, D)
         quant_bytes = 3 * (wl.q_bf16.size + wl.idx_q_bf16.size)
         # indexer bytes: ids written; when some row needs scoring, also the index
-        # query and every index key of the sequence read once
+        # query and every index key of the sequence read once.  Indexer flops:
+        # 2 * 128 per (index head, visible key) of every row with more blocks than k
         nb = pos // PAGE + 1
         index_bytes = ids_h.size * 4
-        if (nb > wl.topk).any():
+        index_scored = bool((nb > wl.topk).any())
+        if index_scored:
             index_bytes += wl.idx_q_bf16.size + int(wl.seq_lens.sum()) * 128
+            index_flops = int((pos[nb > wl.topk] + 1).sum()) * Hidx * 2 * 128
     else:
         idx = wl.indices
         n_valid = int(((idx >= 0) & (idx < wl.kv8.shape[0])).sum())
@@ -407,66 +412,118 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         graph.replay()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
 
-    # per-kernel times: K eager steps with HIP events on the launch stream
-    evs = [new_events() for _ in range(args.steps)]
-    for i in range(args.steps):
+    # per-kernel times: K eager steps with HIP events on the launch stream,
+    # each after a 512 MiB write (outside the events) that evicts the 256 MB
+    # last-level cache, so every input comes from HBM
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    evs = [new_events() for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(float(i))
         step(evs[i])
     torch.cuda.synchronize()
     ms = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in kinds}
     ms.setdefault("index", None)
+    del flush
 
-    ms_step = total_ms / args.steps
+    ms_step = total_ms / steps
     attn_tflops = flops / (ms["attn"] * 1e-3) / 1e12
     value = flops / (ms_step * 1e-3) / 1e12
-    result = {
-        "metric": "fp8 sparse-attn prefill TFLOP/s (% fp8 MFMA peak); indexer top-k GB/s",
+    res = {
         "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 (QK) / bf16 (PV)",
-        "data": "synthetic",
-        "launch": "one captured HIP graph per step, replayed K times; kernels_ms from K eager steps",
         "config": {"workload": wl.name, "tokens": int(T), "q_heads": int(Hq),
-                   "attention_gflop_per_step": round(flops / 1e9, 3),
-                   "parallelism": "single GPU"},
+                   "attention_gflop_per_step": round(flops / 1e9, 3)},
         "kernels_ms": {k: (round(v, 4) if v is not None else None) for k, v in ms.items()},
         "attention_tflops": round(attn_tflops, 3),
         "attention_frac_fp8_peak": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
         "quantize_GBps": round(quant_bytes / (ms["quant"] * 1e-3) / 1e9, 1),
-        "indexer_topk_GBps": (round(index_bytes / (ms["index"] * 1e-3) / 1e9, 1)
-                              if block and ms["index"] else None),
+        "quantize_frac_hbm_peak": round(quant_bytes / (ms["quant"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": committed_traffic(args.workload)},
+                     "traffic": committed_traffic(n)},
     }
+    if block:
+        gbps = index_bytes / (ms["index"] * 1e-3) / 1e9
+        res["indexer_topk_GBps"] = round(gbps, 1)
+        if index_scored:
+            itf = index_flops / (ms["index"] * 1e-3) / 1e12
+            res["indexer_scoring"] = {"gflop": round(index_flops / 1e9, 3), "tflops": round(itf, 3),
+                                      "frac_fp8_peak": round(itf / PEAK_FP8_TFLOPS, 4), "bytes": int(index_bytes)}
+        else:
+            # no row sees more than k blocks: the ids are the closed form, written
+            # without scoring, so the rate is that of an id write
+            res["indexer_topk_note"] = "closed form: no row has more than k blocks, nothing scored"
     if block and wl.max_q_len == 1:
         # decode: one query per sequence, so the attention streams the selected
         # K/V pages and is bound by HBM, not by the matrix cores
         seq, _ = token_positions(wl.cu_seqlens_q, wl.seq_lens)
         dbytes = decode_attention_bytes(ids_h, seq, Hq, Hidx, Hkv, D)
         gbps = dbytes / (ms["attn"] * 1e-3) / 1e9
-        result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                              "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": committed_traffic(args.workload),
-                              "algorithmic_bytes": int(dbytes)}
+        res["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": committed_traffic(n),
+                           "algorithmic_bytes": int(dbytes)}
+        # the decode indexer reads every index key of the batch once
+        res["indexer_topk_frac_hbm_peak"] = round(res["indexer_topk_GBps"] / PEAK_HBM_GBPS, 4)
+    if producers:
+        res["cache_store"] = measure_cache_store(fts, wl, block, steps)
+        if block:
+            res["qknorm_rope_quantize"] = measure_qknorm_rope_quantize(fts, int(T), int(Hidx), steps)
+        else:
+            res["rope_quantize"] = measure_rope_quantize(fts, Q, steps)
+    del graph
+    torch.cuda.synchronize()
+    return res, wl, block
 
-    result["cache_store"] = measure_cache_store(fts, wl, block, args.steps)
-    if block:
-        result["qknorm_rope_quantize"] = measure_qknorm_rope_quantize(fts, int(T), int(Hidx), args.steps)
-    if not block:
-        result["rope_quantize"] = measure_rope_quantize(fts, Q, args.steps)
 
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import torch
+    import fp8_top_sparse_amd as fts
+
+    fts.load()
+    torch.cuda.set_device(0)
+    head, wl, block = run_workload(args.workload, args.steps, args.warmup, producers=True)
+    result = {
+        "metric": "fp8 sparse-attn prefill TFLOP/s (% fp8 MFMA peak); indexer top-k GB/s",
+        "value": head.pop("value"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (QK) / bf16 (PV)",
+        "data": "synthetic",
+        "launch": "one captured HIP graph per step, replayed K times; kernels_ms from K eager steps, "
+                  "each after a 512 MiB cache-evicting write",
+    }
+    result["config"] = dict(head.pop("config"), parallelism="single GPU")
+    result.update(head)
+    if not args.no_extra and args.workload == 3:
+        # the other two headline shapes: long-MLA token-mode prefill and the decode batch
+        extra = {}
+        for n in (4, 5):
+            torch.cuda.empty_cache()
+            r, _, _ = run_workload(n, max(10, args.steps // 2), args.warmup, producers=False)
+            extra[r["config"]["workload"]] = r
+        result["extra_workloads"] = extra
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, block)
     print(json.dumps(result))
@@ -476,7 +533,9 @@ def cpu_baseline(wl, block: bool, min_seconds: float = 10.0, max_tokens: int = 4
     """The CPU oracle (float64, numpy) on a bounded sample of the same workload:
     batches of randomly chosen query tokens go through quantize, indexer and
     attention until at least `min_seconds` of work is done.  `cores` is the
-    parallelism the oracle actually achieved (process CPU time / wall time)."""
+    number of host cores the process may run on (its CPU affinity), which is
+    also the BLAS thread count; `parallelism` is what the oracle achieved
+    (process CPU time / wall time), and `blas` names the BLAS library."""
     import workloads as W  # noqa: F401
     from oracle import attention as OA
     from oracle import indexer as OI
@@ -513,8 +572,19 @@ def cpu_baseline(wl, block: bool, min_seconds: float = 10.0, max_tokens: int = 4
                                  attn_sink=wl.sink, tokens=toks)
             flops += int((wl.indices[toks] >= 0).sum()) * wl.q_bf16.shape[1] * 2 * (576 + wl.d_v)
     dt = time.perf_counter() - wall0
-    cores = max(1, round((time.process_time() - cpu0) / dt))
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    achieved = (time.process_time() - cpu0) / dt
+    blas = {}
+    try:
+        import threadpoolctl
+        for info in threadpoolctl.threadpool_info():
+            if info.get("user_api") == "blas":
+                blas = {"library": info.get("internal_api"), "version": info.get("version"),
+                        "threads": info.get("num_threads")}
+                break
+    except ImportError:
+        pass
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "parallelism": round(achieved, 2), "blas": blas, "kind": "oracle",
             "sample": f"{done} query tokens of {wl.name} (random, all heads) through quantize, indexer and "
                       f"attention (float64 numpy, {dt:.1f} s)"}
 

@@ -127,27 +127,48 @@ def _i32t(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def flatten_to_2d(x: torch.Tensor):
-    """(rows, cols, row_stride) of a tensor whose leading dims flatten onto one stride.
+    """(rows, cols, row_stride) of ``x`` seen as rows of its last dim.
 
-    Raises ValueError when the last dim is not contiguous or the leading dims
-    cannot be expressed with a single row stride.
+    The quantize entry takes any tensor whose last dim is contiguous and whose
+    leading dims collapse onto one row stride, as the fp8 quantize wrapper on
+    the sglang PR 25460 digest does by flattening to 2-D (code excerpt of
+    fp8_quantize.py).  The leading dims are merged from the innermost one
+    outward: each must step by the row stride times the rows merged so far;
+    a dim of size 1 adds no rows and its stride does not matter.  Raises
+    ValueError when the last dim is not contiguous or no single row stride
+    describes the leading dims.
     """
     if x.dim() == 0:
         return 1, 1, 1
-    if x.numel() == 0:
-        return 0, x.shape[-1], x.shape[-1]
-    if x.stride(-1) != 1:
-        raise ValueError(f"last dim must be contiguous (stride {x.stride(-1)})")
     cols = x.shape[-1]
-    if x.dim() == 1:
-        return 1, cols, cols
-    rows = x.numel() // cols if cols else 0
-    row_stride = x.stride(-2)
-    for d in range(x.dim() - 2):
-        expected = x.shape[d + 1] * x.stride(d + 1)
-        if x.shape[d] > 1 and x.stride(d) != expected:
-            raise ValueError(f"cannot flatten dim {d}: stride {x.stride(d)} != {expected}")
-    return rows, cols, row_stride
+    if x.numel() == 0:
+        return 0, cols, cols
+    if cols > 1 and x.stride(-1) != 1:
+        raise ValueError(f"last dim must be contiguous (stride {x.stride(-1)})")
+    rows, row_stride = 1, None
+    for d in range(x.dim() - 2, -1, -1):
+        n, step = x.shape[d], x.stride(d)
+        if n == 1:
+            continue
+        if row_stride is None:
+            row_stride = step
+        elif step != row_stride * rows:
+            raise ValueError(f"cannot flatten dim {d}: stride {step} != {row_stride * rows}")
+        rows *= n
+    return rows, cols, cols if row_stride is None else row_stride
+
+
+def _same_device(what: str, dev: torch.device, *tensors) -> None:
+    """Every given tensor must be a CUDA tensor on ``dev`` (the library takes raw device pointers)."""
+    for t in tensors:
+        if t is not None and (t.device.type != "cuda" or t.device != dev):
+            raise ValueError(f"{what}: every tensor must be on {dev} (got one on {t.device})")
+
+
+def _check_out(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"(got {t.dtype} {tuple(t.shape)})")
 
 
 def fp8_quantize(x: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
@@ -222,13 +243,22 @@ def indexer_topk(idx_q: torch.Tensor, idx_k: torch.Tensor, block_table: torch.Te
     bt = _i32t(block_table, "block_table")
     cu = _i32t(cu_seqlens_q, "cu_seqlens_q")
     sl = _i32t(seq_lens, "seq_lens")
+    if bt.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks]")
     B, max_blocks = bt.shape
+    if cu.numel() != B + 1 or sl.numel() != B:
+        raise ValueError(f"cu_seqlens_q needs batch + 1 = {B + 1} entries and seq_lens {B} "
+                         f"(got {cu.numel()} and {sl.numel()})")
     if out is None:
         out = torch.empty((H, T, topk), dtype=torch.int32, device=q.device)
+    _check_out(out, "out", torch.int32, (H, T, topk))
     need = lib.indexer_topk_workspace_size(T, H, max_blocks)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _same_device("indexer_topk", q.device, q, k, bt, cu, sl, out, workspace)
     _check(lib.indexer_topk(_ptr(q), _ptr(k), pages, _ptr(bt), max_blocks, _ptr(cu), _ptr(sl), B, T,
                             int(max_q_len), H, D, page, float(sm_scale), _scale(idx_q_scale),
                             _scale(idx_k_scale), int(topk), _ptr(out), _ptr(workspace), wsz,
@@ -270,6 +300,12 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
             raise ValueError("token mode: k must be [S, Dqk]")
         num_kv, Hkv, Hidx = kb.shape[0], 1, 1
         Dv = d_v if d_v is not None else (vb.shape[-1] if vb is not None else 512)
+        if kb.shape[1] != Dqk:
+            raise ValueError(f"token mode: k rows hold {kb.shape[1]} bytes, q rows {Dqk}")
+        if vb is not None and (vb.dim() != 2 or tuple(vb.shape) != (num_kv, Dv)):
+            raise ValueError(f"token mode: v must be [{num_kv}, {Dv}] (got {tuple(vb.shape)})")
+        if vb is None and Dv > Dqk:
+            raise ValueError(f"token mode: V = the first {Dv} columns of k needs rows of at least {Dv} bytes")
         if idx.dim() != 2 or idx.shape[0] != T:
             raise ValueError("token mode: indices must be [T, topk]")
         topk = idx.shape[1]
@@ -279,18 +315,29 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
         m = BLOCK_MODE
         if kb.dim() != 4 or vb is None or vb.dim() != 4:
             raise ValueError("block mode: k and v must be [pages, Hkv, page, D]")
-        num_kv, Hkv, page, _ = kb.shape
+        num_kv, Hkv, page, kd = kb.shape
         Dv = vb.shape[-1] if d_v is None else d_v
+        if kd != Dqk:
+            raise ValueError(f"block mode: k rows hold {kd} bytes, q rows {Dqk}")
+        if tuple(vb.shape) != (num_kv, Hkv, page, Dv):
+            raise ValueError(f"block mode: v must be [{num_kv}, {Hkv}, {page}, {Dv}] like k (got {tuple(vb.shape)})")
         if idx.dim() != 3 or idx.shape[1] != T:
             raise ValueError("block mode: indices must be [Hidx, T, topk]")
         Hidx, topk = idx.shape[0], idx.shape[2]
         bt = _i32t(block_table, "block_table")
         cu = _i32t(cu_seqlens_q, "cu_seqlens_q")
         sl = _i32t(seq_lens, "seq_lens")
+        if bt.dim() != 2:
+            raise ValueError("block_table must be [batch, max_blocks]")
         B, max_blocks = bt.shape
+        if cu.numel() != B + 1 or sl.numel() != B:
+            raise ValueError(f"cu_seqlens_q needs batch + 1 = {B + 1} entries and seq_lens {B} "
+                             f"(got {cu.numel()} and {sl.numel()})")
     else:
         raise ValueError(f"mode must be 'token' or 'block', got {mode!r}")
     tl = None if topk_length is None else _i32t(topk_length, "topk_length")
+    if tl is not None and tl.numel() != T:
+        raise ValueError(f"topk_length needs one entry per query token ({T}, got {tl.numel()})")
     sink = None
     if attn_sink is not None:
         if attn_sink.dtype != torch.float32 or attn_sink.numel() != Hq:
@@ -303,10 +350,16 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
         max_logits = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    _check_out(out, "out", torch.bfloat16, (T, Hq, Dv))
+    _check_out(max_logits, "max_logits", torch.float32, (T, Hq))
+    _check_out(lse, "lse", torch.float32, (T, Hq))
     need = lib.sparse_attn_workspace_size(m, B, T, int(max_q_len), Hq, Hkv, Hidx, Dv, topk, max_blocks)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _same_device("sparse_attn_fwd", dev, qb, kb, vb, idx, tl, bt, cu, sl, sink, out, max_logits, lse, workspace)
     _check(lib.sparse_attn_fwd(m, _ptr(qb), _ptr(kb), _ptr(vb), num_kv, _ptr(idx), topk, _ptr(tl), _ptr(bt),
                                max_blocks, _ptr(cu), _ptr(sl), B, T, int(max_q_len), Hq, Hkv, Hidx, Dqk, Dv,
                                page, float(sm_scale), _scale(q_scale), _scale(k_scale), _scale(v_scale),

@@ -38,11 +38,9 @@
 namespace fp8ts {
 namespace {
 
-#ifndef FP8TS_BLOCK_WAVES
-#define FP8TS_BLOCK_WAVES 8
-#endif
-// block-mode prefill: waves per 256-row workgroup (4 x 64 rows or 8 x 32 rows)
-constexpr int kPrefillWaves = FP8TS_BLOCK_WAVES;
+// block-mode prefill whose block bitmaps leave no room for the pipelined
+// kernel's two K/V buffers: 8 waves x 32 rows per 256-row workgroup
+constexpr int kPrefillWaves = 8;
 
 // Dynamic LDS layout sizes.
 template <int DQK, int DV, int KT>
@@ -487,18 +485,12 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
 }
 
 // ---------------------------------------------------------------- host side
-#ifndef FP8TS_DECODE_CHUNK
-#define FP8TS_DECODE_CHUNK 32
-#endif
-constexpr int kDecodeChunk = FP8TS_DECODE_CHUNK;   // union blocks per decode workgroup
-#ifndef FP8TS_STREAM_CHUNK
-#define FP8TS_STREAM_CHUNK 32
-#endif
-constexpr int kStreamChunk = FP8TS_STREAM_CHUNK;   // union blocks per streamed-decode workgroup (0: off)
+constexpr int kDecodeChunk = 32;   // union blocks per tile-decode workgroup
+constexpr int kStreamChunk = 32;   // union blocks per streamed-decode workgroup
 
 struct Plan {
-  int kind;   // 0 block prefill, 1 block decode, 2 token 128 heads, 3 token 16 heads,
-              // 4 block prefill, pipelined, 5 block decode, pipelined,
+  int kind;   // 0 block prefill (single-buffered), 2 token 128 heads, 3 token 16 heads,
+              // 4 block prefill, pipelined, 5 block decode, tile kernel,
               // 6 token 128 heads, pipelined, 7 block decode, streamed per wave
   Grid gr;
   int64_t nblocks;
@@ -519,85 +511,61 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
     gr.G = hq / hkv;
     gr.gqi = hq / hidx;
     gr.W = (max_blocks + 31) / 32;
-    // few query rows per sequence (decode): 64-row tiles, every wave loads,
-    // only the waves owning valid rows compute; the block union is split
-    // across workgroups to fill the GPU
+    // few query rows per sequence (decode): tiles of at most 64 rows whose
+    // block union is split across workgroups to fill the GPU
     const bool decode = (int64_t)max_q_len * gr.G <= 64;
-    const int rows = decode ? 64 : block_prefill_rows();
+    const int rows = decode ? block_decode_rows() : block_prefill_rows();
     gr.TT = rows / gr.G;
     if (gr.TT < 1) gr.TT = 1;
     gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
     // index heads touched by the q heads of one kv head
-    const int gi_lo = 0, gi_hi = (gr.G - 1) / gr.gqi;
     gr.n_il = gr.G >= gr.gqi ? gr.G / gr.gqi : 1;
-    (void)gi_lo;
-    (void)gi_hi;
     gr.NL = gr.TT * gr.n_il;
     if (decode) {
-      pl.kind = 1;
-      // split the union (at most n_il * topk blocks) into chunks of ~8 blocks
-      int ubound = gr.n_il * topk;
+      // decode tiles (at most 64 rows): the tile kernel streams ~kDecodeChunk
+      // blocks of the union per workgroup (small single-buffered tiles,
+      // several workgroups per CU); its LDS fits any table of up to 4096
+      // blocks
+      pl.kind = 5;
+      int ubound = gr.n_il * (gr.TT < max_q_len ? gr.TT : max_q_len) * topk;
       if (ubound > max_blocks) ubound = max_blocks;
-      gr.splits = (ubound + 7) / 8;
+      gr.splits = (ubound + kDecodeChunk - 1) / kDecodeChunk;
       if (gr.splits < 1) gr.splits = 1;
+      pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+      pl.lds = block_decode_lds(gr);
+      // decode tiles of at most 16 rows: the streamed decode kernel, every
+      // wave walking its own share of ~kStreamChunk blocks of the union
+      if (gr.G <= 16 && 16 % gr.G == 0 && (int64_t)max_q_len * gr.G <= 16) {
+        Grid sg = gr;
+        sg.TT = 16 / sg.G;
+        sg.n_tiles = (max_q_len + sg.TT - 1) / sg.TT;
+        sg.NL = sg.TT * sg.n_il;
+        int sbound = sg.n_il * (sg.TT < max_q_len ? sg.TT : max_q_len) * topk;
+        if (sbound > max_blocks) sbound = max_blocks;
+        sg.splits = (sbound + kStreamChunk - 1) / kStreamChunk;
+        if (sg.splits < 1) sg.splits = 1;
+        if (block_stream_decode_lds(sg) <= kMaxLds) {
+          gr = sg;
+          pl.kind = 7;
+          pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
+          pl.lds = block_stream_decode_lds(gr);
+        }
+      }
     } else {
       pl.kind = 0;
+      pl.nblocks = (int64_t)batch * hkv * gr.n_tiles;
+      pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
     }
-    pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
-    pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
-    // decode: the pipelined decode kernel (small single-buffered tiles, several
-    // workgroups per CU) streams ~kDecodeChunk blocks of the union per workgroup
-    if (kDecodeChunk > 0 && pl.kind == 1) {
-      Grid dg = gr;
-      dg.TT = block_decode_rows() / gr.G > 0 ? block_decode_rows() / gr.G : 1;
-      dg.n_tiles = (max_q_len + dg.TT - 1) / dg.TT;
-      dg.NL = dg.TT * dg.n_il;
-      int ubound = dg.n_il * (dg.TT < max_q_len ? dg.TT : max_q_len) * topk;
-      if (ubound > max_blocks) ubound = max_blocks;
-      dg.splits = (ubound + kDecodeChunk - 1) / kDecodeChunk;
-      if (dg.splits < 1) dg.splits = 1;
-      if (block_decode_rows() >= gr.G && block_decode_lds(dg) <= kMaxLds) {
-        gr = dg;
-        pl.kind = 5;
-        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
-        pl.lds = block_decode_lds(gr);
-      }
-    }
-    // decode tiles of at most 16 rows: the streamed decode kernel, every wave
-    // walking its own share of ~kStreamChunk blocks of the union
-    if (kStreamChunk > 0 && decode && gr.G <= 16 && 16 % gr.G == 0 && (int64_t)max_q_len * gr.G <= 16) {
-      Grid sg = pl.gr;
-      sg.TT = 16 / sg.G;
-      sg.n_tiles = (max_q_len + sg.TT - 1) / sg.TT;
-      sg.NL = sg.TT * sg.n_il;
-      int ubound = sg.n_il * (sg.TT < max_q_len ? sg.TT : max_q_len) * topk;
-      if (ubound > max_blocks) ubound = max_blocks;
-      sg.splits = (ubound + kStreamChunk - 1) / kStreamChunk;
-      if (sg.splits < 1) sg.splits = 1;
-      if (block_stream_decode_lds(sg) <= kMaxLds) {
-        gr = sg;
-        pl.kind = 7;
-        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
-        pl.lds = block_stream_decode_lds(gr);
-      }
-    }
-    // prefill tiles go to the pipelined kernel when its LDS fits; otherwise to
-    // the single-buffered one, whose tiles are 256 rows
-    if (pl.kind == 0) {
-      if (block_prefill_lds(gr) <= kMaxLds) {
-        pl.kind = 4;
-        pl.lds = block_prefill_lds(gr);
-        // sequences spanning several tiles visit each page many times over:
-        // convert every V page to its V^T tile once, up front
-        const size_t vt = (size_t)batch * max_blocks * hkv * vt_page_bytes();
-        if (gr.n_tiles >= 4 && vt <= ((size_t)1 << 30)) pl.vt_bytes = vt;
-      } else if (gr.TT != 256 / gr.G) {
-        gr.TT = 256 / gr.G > 0 ? 256 / gr.G : 1;
-        gr.n_tiles = (max_q_len + gr.TT - 1) / gr.TT;
-        gr.NL = gr.TT * gr.n_il;
-        pl.nblocks = (int64_t)gr.splits * batch * hkv * gr.n_tiles;
-        pl.lds = lds_base<128, 128, 128>() + 4 * ((size_t)(gr.NL + 1) * gr.W + 4 + (size_t)gr.W * 32);
-      }
+    // prefill tiles go to the pipelined kernel when its LDS fits; otherwise
+    // (block tables of about 4000 blocks) to the single-buffered one, whose
+    // tiles are the same 256 rows
+    if (pl.kind == 0 && block_prefill_lds(gr) <= kMaxLds) {
+      pl.kind = 4;
+      pl.lds = block_prefill_lds(gr);
+      // sequences spanning several tiles visit each page many times over:
+      // convert every V page to its V^T tile once, up front
+      const size_t vt = (size_t)batch * max_blocks * hkv * vt_page_bytes();
+      if (gr.n_tiles >= 4 && vt <= ((size_t)1 << 30)) pl.vt_bytes = vt;
     }
   } else {
     if (hq % token_mla_rows() == 0) {
@@ -677,9 +645,12 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
   switch (pl.kind) {
     case 0: st = launch_k(attn_kernel<128, 128, kPrefillWaves, 16 / kPrefillWaves, 128, true>, pl,
                           kPrefillWaves * 64, a, stream); break;
-    case 1: st = launch_k(attn_kernel<128, 128, 4, 1, 128, true>, pl, 256, a, stream); break;
     case 4: st = launch_block_prefill(a, pl.gr, pl.nblocks, stream); break;
-    case 5: st = launch_block_decode(a, pl.gr, pl.nblocks, stream); break;
+    case 5:
+      if (pl.lds > kMaxLds)
+        return fail(FP8TS_EUNSUPPORTED, "sparse_attn_fwd: decode block lists need %zu bytes of LDS", pl.lds);
+      st = launch_block_decode(a, pl.gr, pl.nblocks, stream);
+      break;
     case 7: st = launch_block_stream_decode(a, pl.gr, pl.nblocks, stream); break;
     case 6:
       if (token_mla_fits(a)) {

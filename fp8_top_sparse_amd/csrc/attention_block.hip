@@ -43,18 +43,6 @@
 namespace fp8ts {
 namespace {
 
-#ifndef FP8TS_PV_AHEAD
-#define FP8TS_PV_AHEAD 2
-#endif
-#ifndef FP8TS_PREFILL_ROWS
-#define FP8TS_PREFILL_ROWS 256
-#endif
-#ifndef FP8TS_PREFILL_BUFS
-#define FP8TS_PREFILL_BUFS 2
-#endif
-#ifndef FP8TS_PREFILL_WAVES
-#define FP8TS_PREFILL_WAVES 8
-#endif
 constexpr int kD = 128;
 constexpr int kNdt = kD / 16;             // 16-dim output tiles
 // K and V^T tiles are stored in MFMA operand order: every operand fetch is
@@ -90,20 +78,17 @@ struct Cfg {
 };
 // prefill: 256-row tiles, 8 waves of 32 rows (each K or V^T operand read
 // feeds two MFMAs), double-buffered
-using PrefillCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, FP8TS_PREFILL_BUFS>;
-using PrefillPreCfg = Cfg<FP8TS_PREFILL_WAVES, FP8TS_PREFILL_ROWS, 2, true>;
+using PrefillCfg = Cfg<8, 256, 2>;
+using PrefillPreCfg = Cfg<8, 256, 2, true>;
 // the same 256-row tile as 16 waves of 16 rows, for prompts whose rows select
 // only part of their causal blocks: a wave skips every block that none of
 // its 16 rows selected, which happens more often than for 32 rows (32k
 // prompt, top-64: 3.164 ms against 3.23 ms; a prompt whose rows select every
 // causal block, as at 8k, runs 5% slower on it)
-using PrefillPreSparseCfg = Cfg<16, FP8TS_PREFILL_ROWS, 2, true>;
+using PrefillPreSparseCfg = Cfg<16, 256, 2, true>;
 // decode: few rows per kv head, so small single-buffered workgroups that
 // share a CU keep more pages in flight
-#ifndef FP8TS_DECODE_WAVES
-#define FP8TS_DECODE_WAVES 4
-#endif
-using DecodeCfg = Cfg<FP8TS_DECODE_WAVES, FP8TS_DECODE_WAVES * 16, 1>;
+using DecodeCfg = Cfg<4, 64, 1>;
 
 // V staging unit u (0..1023) of a 128-key x 128-dim tile: 4 dims x 4 keys,
 // half jh = u & 1 of V^T chunk cix = u >> 6, dims 4 d4 .. + 3 with
@@ -485,7 +470,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           }
           // V^T operand reads run kPvAhead MFMA groups ahead (the DMA-staged
           // configuration has the registers for more reads in flight)
-          constexpr int kPvAhead = C::kPre ? 4 : FP8TS_PV_AHEAD;
+          constexpr int kPvAhead = C::kPre ? 4 : 2;
           __builtin_amdgcn_sched_group_barrier(0x100, kPvAhead, 0);
           sched_mfma_then_reads<2 * kNdt - kPvAhead, kCols, 1>();
           sched_mfma_then_reads<kPvAhead, kCols, 0>();

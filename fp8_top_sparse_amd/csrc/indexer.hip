@@ -62,17 +62,12 @@ __device__ __forceinline__ SeqInfo find_seq(const int32_t *cu, const int32_t *sl
 
 // ------------------------------------------------------------ score kernel
 // CT column tiles of 16 rows; rows = tokens x heads (row r: token r / H, head r % H).
-#ifndef FP8TS_IDX_DEC_LDS
-#define FP8TS_IDX_DEC_LDS 1
-#endif
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int CT>
 __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n_tiles, int splits) {
-#if FP8TS_IDX_DEC_LDS
   // each wave's page, copied linearly (a 1 KB contiguous read per wave load)
   __shared__ __attribute__((aligned(16))) uint8_t kpage[4][kPage * kD];
-#endif
   const int H = a.num_heads;
   constexpr int ROWS = CT * 16;
   const int TT = ROWS / H;                       // tokens per workgroup tile
@@ -135,7 +130,6 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
     if (page >= 0 && page < a.num_pages) {
       const uint8_t *kp = a.idx_k + (int64_t)page * kPage * kD;
       v8i ka[8];
-#if FP8TS_IDX_DEC_LDS
       // Loading straight into MFMA operand order makes every wave load 16 rows
       // x 64 bytes; random pages read that way stream at about 5.1 TB/s
       // against 5.9 TB/s for 1 KB contiguous wave loads.  So the page is
@@ -154,15 +148,6 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
         v4i lo = src[0], hi = src[1];
         ka[kt] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-#else
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const v4i *src = reinterpret_cast<const v4i *>(kp + (kt * 16 + col) * kD + 32 * g);
-        v4i lo = __builtin_nontemporal_load(src);
-        v4i hi = __builtin_nontemporal_load(src + 1);
-        ka[kt] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#endif
       const int key0 = blk * kPage;
       const bool causal = key0 + kPage - 1 > p_min;   // wave-uniform
 #pragma unroll
@@ -211,10 +196,7 @@ constexpr int kScPitch = kFlush + 1;          // floats per row of the score buf
 // pages per workgroup: a tile's causal page range is split into chunks of
 // kSChunk pages, so the grid holds many similar workgroups instead of one
 // per tile (a 32k prompt would otherwise give 384 workgroups of 65..256 pages)
-#ifndef FP8TS_IDX_SCHUNK
-#define FP8TS_IDX_SCHUNK 32
-#endif
-constexpr int kSChunk = FP8TS_IDX_SCHUNK;
+constexpr int kSChunk = 32;
 
 __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles,
                                                                               int n_chunks) {

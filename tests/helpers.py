@@ -96,3 +96,26 @@ def workload(n: int):
     if n not in _WL_CACHE:
         _WL_CACHE[n] = W.workload(n)
     return _WL_CACHE[n]
+
+
+_IDS_CACHE = {}
+
+
+def exact_workload_ids(n: int):
+    """(exact-mode index query codes, index-key codes, oracle ids [Hidx, T, k])
+    of full-size block workload ``n`` (3: 32k prefill, 5: 64 x 32k decode),
+    every row computed by the oracle and cached for the session (about 20 s
+    of float64 scoring for the 32k prompt)."""
+    import workloads as W
+    from oracle import indexer as OI
+    if n not in _IDS_CACHE:
+        wl = workload(n)
+        if "idx_q8_exact" in wl.extra:
+            iq, ik = wl.extra["idx_q8_exact"], wl.extra["idx_k8_exact"]
+        else:
+            iq, ik = W.exact_index_codes(1000 + n, wl.idx_q_bf16.shape[0], wl.idx_q_bf16.shape[1],
+                                         wl.idx_q_bf16.shape[2], wl.idx_k8.shape[0])
+        ids = OI.indexer_topk(iq, ik, wl.block_table, wl.cu_seqlens_q, wl.seq_lens, sm_scale=wl.idx_sm_scale,
+                              idx_q_scale=wl.idx_q_scale, idx_k_scale=wl.idx_k_scale, topk=wl.topk)
+        _IDS_CACHE[n] = (iq, ik, ids)
+    return _IDS_CACHE[n]

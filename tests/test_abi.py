@@ -311,10 +311,94 @@ def test_flatten_to_2d():
     assert fts.flatten_to_2d(x) == (12, 8, 8)
     y = torch.empty(4, 3, 16)[..., :8]
     assert fts.flatten_to_2d(y) == (12, 8, 16)
+    z = torch.empty(5, 7, 3, 32)[:, :, :, :8]                  # rows of 8 at a 32-element stride
+    assert fts.flatten_to_2d(z) == (105, 8, 32)
+    assert fts.flatten_to_2d(torch.empty(1, 6, 8)) == (6, 8, 8)
+    assert fts.flatten_to_2d(torch.empty(6, 1, 8)[:, :, :]) == (6, 8, 8)
+    # a size-1 dim adds no rows, whatever its stride
+    w = torch.empty(6, 16).as_strided((6, 1, 8), (16, 999, 1))
+    assert fts.flatten_to_2d(w) == (6, 8, 16)
+    assert fts.flatten_to_2d(torch.empty(8)) == (1, 8, 8)
+    assert fts.flatten_to_2d(torch.empty(0, 4, 8)) == (0, 8, 8)
     with pytest.raises(ValueError):
         fts.flatten_to_2d(torch.empty(8, 4).t())
     with pytest.raises(ValueError):
         fts.flatten_to_2d(torch.empty(4, 6, 8)[:, :3, :])
+    with pytest.raises(ValueError):
+        fts.flatten_to_2d(torch.empty(3, 4, 8).transpose(0, 1))
+
+
+# The binding checks what the C ABI cannot see (tensor shapes, dtypes and
+# devices) before anything reaches the library; these run on CPU tensors,
+# which fail on the shape checks before the device check.
+def _block_args(**over):
+    T, Hq, Hkv, Hidx, P, D, B, MB, k = 10, 16, 2, 4, 5, 128, 2, 3, 4
+    a = dict(q=torch.zeros(T, Hq, D, dtype=torch.uint8), k=torch.zeros(P, Hkv, 128, D, dtype=torch.uint8),
+             indices=torch.zeros(Hidx, T, k, dtype=torch.int32), v=torch.zeros(P, Hkv, 128, D, dtype=torch.uint8),
+             block_table=torch.zeros(B, MB, dtype=torch.int32), cu_seqlens_q=torch.tensor([0, 4, 10], dtype=torch.int32),
+             seq_lens=torch.tensor([4, 6], dtype=torch.int32))
+    a.update(over)
+    return a
+
+
+def _run_block(a, **kw):
+    return fts.sparse_attn_fwd(a["q"], a["k"], a["indices"], sm_scale=0.1, mode="block", v=a["v"],
+                               block_table=a["block_table"], cu_seqlens_q=a["cu_seqlens_q"],
+                               seq_lens=a["seq_lens"], max_q_len=6, **kw)
+
+
+def test_binding_rejects_mismatched_block_tensors(lib):
+    with pytest.raises(ValueError, match="k rows hold 64"):
+        _run_block(_block_args(k=torch.zeros(5, 2, 128, 64, dtype=torch.uint8)))
+    with pytest.raises(ValueError, match="v must be"):
+        _run_block(_block_args(v=torch.zeros(4, 2, 128, 128, dtype=torch.uint8)))
+    with pytest.raises(ValueError, match="v must be"):
+        _run_block(_block_args(v=torch.zeros(5, 1, 128, 128, dtype=torch.uint8)))
+    with pytest.raises(ValueError, match="cu_seqlens_q needs"):
+        _run_block(_block_args(cu_seqlens_q=torch.tensor([0, 10], dtype=torch.int32)))
+    with pytest.raises(ValueError, match="seq_lens"):
+        _run_block(_block_args(seq_lens=torch.tensor([4, 6, 1], dtype=torch.int32)))
+    with pytest.raises(ValueError, match="out must be"):
+        _run_block(_block_args(), out=torch.zeros(10, 16, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        _run_block(_block_args(), out=torch.zeros(10, 16, 128, dtype=torch.float32))
+    with pytest.raises(ValueError, match="max_logits must be"):
+        _run_block(_block_args(), max_logits=torch.zeros(10, 8, dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse must be"):
+        _run_block(_block_args(), lse=torch.zeros(16, 10, dtype=torch.float32).t())
+    # every shape right: the CPU tensors then fail the device check
+    with pytest.raises(ValueError, match="must be on"):
+        _run_block(_block_args())
+
+
+def test_binding_rejects_mismatched_token_tensors(lib):
+    q = torch.zeros(3, 16, 576, dtype=torch.uint8)
+    idx = torch.zeros(3, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k rows hold 512"):
+        fts.sparse_attn_fwd(q, torch.zeros(100, 512, dtype=torch.uint8), idx, sm_scale=0.1)
+    with pytest.raises(ValueError, match="v must be"):
+        fts.sparse_attn_fwd(q, torch.zeros(100, 576, dtype=torch.uint8), idx, sm_scale=0.1,
+                            v=torch.zeros(99, 512, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="topk_length"):
+        fts.sparse_attn_fwd(q, torch.zeros(100, 576, dtype=torch.uint8), idx, sm_scale=0.1,
+                            topk_length=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="must be on"):
+        fts.sparse_attn_fwd(q, torch.zeros(100, 576, dtype=torch.uint8), idx, sm_scale=0.1)
+
+
+def test_binding_rejects_mismatched_indexer_tensors(lib):
+    iq = torch.zeros(10, 4, 128, dtype=torch.uint8)
+    ik = torch.zeros(5, 128, 128, dtype=torch.uint8)
+    bt = torch.zeros(2, 3, dtype=torch.int32)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    sl = torch.tensor([4, 6], dtype=torch.int32)
+    with pytest.raises(ValueError, match="cu_seqlens_q needs"):
+        fts.indexer_topk(iq, ik, bt, cu[:2], sl, max_q_len=6, sm_scale=0.1, topk=4)
+    with pytest.raises(ValueError, match="out must be"):
+        fts.indexer_topk(iq, ik, bt, cu, sl, max_q_len=6, sm_scale=0.1, topk=4,
+                         out=torch.zeros(4, 10, 8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="must be on"):
+        fts.indexer_topk(iq, ik, bt, cu, sl, max_q_len=6, sm_scale=0.1, topk=4)
 
 
 def test_binding_maps_status_to_python_errors(lib):

@@ -16,7 +16,7 @@ from oracle import e4m3
 from oracle import indexer as OI
 from oracle import quantize as OQ
 import workloads as W
-from helpers import assert_attention_close, bf16_dev, dev, host, workload
+from helpers import assert_attention_close, bf16_dev, dev, exact_workload_ids, host, workload
 
 pytestmark = pytest.mark.gpu
 PAGE = 128
@@ -385,29 +385,17 @@ def test_block_prefill_late_large_logits(gpu):
     assert_attention_close(got, ref, "late large logits")
 
 
-@pytest.mark.parametrize("n", [2, 3])
-def test_block_prefill_full_size_sampled(gpu, n):
-    """8k / 32k causal prefill at full size, ids from the oracle indexer."""
-    wl = workload(n)
+def test_block_prefill_8k_full_size_sampled(gpu):
+    """8k causal prefill at full size: every row selects all of its causal
+    blocks (the closed-form ids), so the attention is dense causal."""
+    wl = workload(2)
     q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
-    iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
     T = q8.shape[0]
-    rng = np.random.default_rng(n)
-    toks = np.sort(np.concatenate([rng.choice(T, 10, replace=False), [0, 1, T - 1]]))
-    toks = np.unique(toks)
-    # full id tensor: padding branch rows in closed form, scored rows by the oracle
-    ids = np.empty((4, T, wl.topk), np.int32)
     nb = np.arange(T) // PAGE + 1
-    ids[:] = np.where(np.arange(wl.topk)[None, :] < nb[:, None], np.arange(wl.topk)[None, :], -1)[None]
-    scored = np.nonzero(nb > wl.topk)[0]
-    if len(scored):
-        # rows that are not sampled keep a valid but arbitrary selection (the first k blocks)
-        ids[:, scored] = np.arange(wl.topk)[None, None, :]
-        need = toks[nb[toks] > wl.topk]
-        if len(need):
-            ids[:, need] = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
-                                           sm_scale=wl.idx_sm_scale, idx_q_scale=wl.idx_q_scale,
-                                           idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=need)
+    ids = np.where(np.arange(wl.topk)[None, :] < nb[:, None], np.arange(wl.topk)[None, :], -1)
+    ids = np.ascontiguousarray(np.broadcast_to(ids[None], (4, T, wl.topk)).astype(np.int32))
+    toks = np.unique(np.concatenate([np.random.default_rng(2).choice(T, 40, replace=False),
+                                     [0, 1, 31, 32, 127, 128, T - 1]]))
     got = gpu.sparse_attn_fwd(dev(q8), dev(wl.k_cache8), dev(ids), v=dev(wl.v_cache8), sm_scale=wl.sm_scale,
                               mode="block", block_table=dev(wl.block_table), cu_seqlens_q=dev(wl.cu_seqlens_q),
                               seq_lens=dev(wl.seq_lens), max_q_len=wl.max_q_len, q_scale=wl.q_scale,
@@ -416,25 +404,47 @@ def test_block_prefill_full_size_sampled(gpu, n):
                                sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
                                v_scale=wl.v_scale, tokens=toks)
     out, ml, lse = got
-    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, f"workload {n}")
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "workload 2")
 
 
-def test_block_decode_full_size_sampled(gpu):
-    """Decode: 64 sequences x 32k tokens, top-64 blocks per index head."""
-    wl = workload(5)
+def test_block_prefill_32k_full_size_oracle_ids(gpu):
+    """32k causal prefill at full size with U(0.1, 4) scales, on the oracle's
+    complete id tensor for the exact-mode index codes (every row's own top-64,
+    so every query tile walks the block unions the bench meets).  96 rows
+    compared, spread over tile positions: the first, last and middle rows of
+    32-token tiles, rows at 128-token block edges, and random rows."""
+    wl = workload(3)
+    _, _, ids = exact_workload_ids(3)
     q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
-    iq8 = OQ.quantize(wl.idx_q_bf16, OQ.BF16, wl.idx_q_scale)
-    seqs = [0, 17, 63]
-    ids = np.tile(np.arange(wl.topk, dtype=np.int32), (4, 64, 1))
-    ids[:, seqs] = OI.indexer_topk(iq8, wl.idx_k8, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
-                                   sm_scale=wl.idx_sm_scale, topk=wl.topk, tokens=seqs)
+    T = q8.shape[0]
+    rng = np.random.default_rng(3)
+    tiles = rng.choice(T // 32, 24, replace=False) * 32
+    toks = np.unique(np.concatenate([tiles, tiles + 31, tiles + 15, [0, 127, 128, 8191, 8192, 8319, T - 1],
+                                     rng.choice(T, 40, replace=False)]))
+    assert len(toks) >= 64
+    got = gpu.sparse_attn_fwd(dev(q8), dev(wl.k_cache8), dev(ids), v=dev(wl.v_cache8), sm_scale=wl.sm_scale,
+                              mode="block", block_table=dev(wl.block_table), cu_seqlens_q=dev(wl.cu_seqlens_q),
+                              seq_lens=dev(wl.seq_lens), max_q_len=wl.max_q_len, q_scale=wl.q_scale,
+                              k_scale=wl.k_scale, v_scale=wl.v_scale)
+    ref = OA.sparse_attn_block(q8, wl.k_cache8, wl.v_cache8, ids, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
+                               sm_scale=wl.sm_scale, q_scale=wl.q_scale, k_scale=wl.k_scale,
+                               v_scale=wl.v_scale, tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "workload 3")
+
+
+def test_block_decode_full_size_oracle_ids(gpu):
+    """Decode: 64 sequences x 32k tokens, every sequence on the oracle's top-64
+    blocks of the exact-mode index codes, all 64 x 16 rows compared."""
+    wl = workload(5)
+    _, _, ids = exact_workload_ids(5)
+    q8 = OQ.quantize(wl.q_bf16, OQ.BF16, wl.q_scale)
     got = gpu.sparse_attn_fwd(dev(q8), dev(wl.k_cache8), dev(ids), v=dev(wl.v_cache8), sm_scale=wl.sm_scale,
                               mode="block", block_table=dev(wl.block_table), cu_seqlens_q=dev(wl.cu_seqlens_q),
                               seq_lens=dev(wl.seq_lens), max_q_len=1)
     ref = OA.sparse_attn_block(q8, wl.k_cache8, wl.v_cache8, ids, wl.block_table, wl.cu_seqlens_q, wl.seq_lens,
-                               sm_scale=wl.sm_scale, tokens=seqs)
-    out, ml, lse = got
-    assert_attention_close((out[seqs], ml[seqs], lse[seqs]), ref, "decode full")
+                               sm_scale=wl.sm_scale)
+    assert_attention_close(got, ref, "decode full")
 
 
 # Decode tiles of at most 16 rows (q heads per kv head x query tokens) run the
@@ -498,3 +508,149 @@ def test_block_decode_streamed_late_large_logits(gpu):
     ref = ref_block(c)
     assert ref[2].max() > 64 * math.log(2) + 5    # far beyond the tiny blocks that start each share
     assert_attention_close(got, ref, "decode late large logits")
+
+
+# Decode tiles of more than 16 rows (q heads per kv head x query tokens of a
+# sequence, at most 64) run the tile kernel with 4 waves x 16 rows; the block
+# union is split over workgroups and the partials merged by the combine kernel.
+@pytest.mark.parametrize("Hq,Hkv,Hidx,q_len", [(16, 2, 4, 3), (16, 2, 4, 4), (16, 2, 4, 8), (32, 1, 8, 1),
+                                               (64, 1, 16, 1), (12, 4, 4, 1)])
+def test_block_decode_tile_head_layouts(gpu, Hq, Hkv, Hidx, q_len):
+    rng = np.random.default_rng(Hq * 1000 + Hkv * 10 + q_len)
+    seq = [int(x) for x in rng.integers(q_len, 9000, 7)] + [q_len, 128 + q_len, 8192]
+    c = block_case(seq, [q_len] * len(seq), seed=Hq + Hkv + q_len, topk=24, Hq=Hq, Hkv=Hkv, Hidx=Hidx, sink=True)
+    c["ids"] = c["ids"].copy()
+    c["ids"][:, q_len:2 * q_len] = -1           # a sequence whose rows selected nothing
+    c["ids"][0, 0, :3] = 5000                   # ids beyond the table: absent
+    got = run_block(gpu, c, q_scale=0.9, k_scale=1.1, v_scale=2.0)
+    ref = ref_block(c, q_scale=0.9, k_scale=1.1, v_scale=2.0)
+    assert_attention_close(got, ref, f"tile decode Hq={Hq} Hkv={Hkv} Hidx={Hidx} q_len={q_len}")
+    out, ml, lse = (host(x) for x in got)
+    assert np.all(out[q_len:2 * q_len] == 0) and np.all(np.isneginf(ml[q_len:2 * q_len]))
+    assert np.all(np.isfinite(lse[q_len:2 * q_len]))      # the sink alone
+
+
+@pytest.mark.parametrize("topk", [1, 7, 8, 9, 16, 17, 33, 64])
+def test_block_decode_tile_split_edges(gpu, topk):
+    """Multi-token decode (4 queries x 8 q heads per kv head = 32 rows): union
+    sizes just below, at and above one workgroup's 32 blocks."""
+    seq = [4, 100, 4000, 9000, 16000, 30000]
+    c = block_case(seq, [4] * len(seq), seed=200 + topk, topk=topk)
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert_attention_close(got, ref, f"tile decode k={topk}")
+
+
+def test_block_decode_tile_late_large_logits(gpu):
+    """Tile decode rows whose first blocks carry tiny logits and a later block
+    logits far above them: the workgroup reruns its share with the exact maxima."""
+    seq = [1500, 2000]
+    c = block_case(seq, [4, 4], seed=47, topk=12)
+    rng = np.random.default_rng(47)
+    kc = c["kc"].copy()
+    for b in range(2):
+        bt = c["bt"][b]
+        kc[bt[:8]] = rand_codes(rng, (8,) + kc.shape[1:], 0.02)
+        kc[bt[10]] = 0
+        kc[bt[10], :, :, 0] = W.e4m3_codes(rng.uniform(256, 448, kc.shape[1:3]).astype(np.float32))
+    c["kc"] = kc
+    c["ids"] = np.broadcast_to(np.arange(12, dtype=np.int32)[None, None], (4, 8, 12)).copy()
+    got = run_block(gpu, c)
+    ref = ref_block(c)
+    assert ref[2].max() > 64 * math.log(2) + 5
+    assert_attention_close(got, ref, "tile decode late large logits")
+
+
+@pytest.mark.parametrize("q_lens", [[2500], [100], [1], [4]])
+def test_block_pages_outside_the_cache_add_no_keys(gpu, q_lens):
+    """Selected blocks whose table entry is -1, one past the cache or far past
+    it add no keys, against the oracle: prefill with the V^T pre-pass (2500
+    queries) and with in-kernel V conversion (100), streamed decode (1) and
+    tile decode (4 queries x 8 heads)."""
+    c = block_case([2500], q_lens, seed=50 + q_lens[0], topk=8, sink=True)
+    P = c["kc"].shape[0]
+    c["bt"] = c["bt"].copy()
+    c["bt"][0, [1, 5, 9]] = [-1, P, 10_000_000]
+    ids = c["ids"].copy()
+    ids[:, :, 0] = 1                 # every row selects block 1
+    ids[0, :, 1] = 5
+    ids[1, :, 1] = 9
+    c["ids"] = ids
+    got = run_block(gpu, c, q_scale=1.2, v_scale=0.5)
+    ref = ref_block(c, q_scale=1.2, v_scale=0.5)
+    assert_attention_close(got, ref, f"absent pages q_len={q_lens[0]}")
+
+
+def test_block_prefill_wide_block_table(gpu):
+    """A 4096-column block table: the per-list bitmaps no longer fit beside two
+    K/V buffers, so the prefill runs the single-buffered tile kernel."""
+    c = block_case([3000, 2100], [1500, 2100], seed=60, topk=8, sink=True)
+    bt = np.full((2, 4096), -1, np.int32)
+    bt[:, :c["bt"].shape[1]] = c["bt"]
+    c["bt"] = bt
+    got = run_block(gpu, c, q_scale=0.8, k_scale=1.2, v_scale=1.5)
+    toks = np.arange(0, 3600, 5)
+    ref = ref_block(c, tokens=toks, q_scale=0.8, k_scale=1.2, v_scale=1.5)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "wide block table")
+
+
+def test_block_prefill_128_q_heads_per_kv_head(gpu):
+    """128 q heads on one kv head (8 index heads): two tokens per 256-row tile."""
+    c = block_case([700], [700], seed=61, topk=3, Hq=128, Hkv=1, Hidx=8, sink=True)
+    got = run_block(gpu, c)
+    toks = np.arange(0, 700, 7)
+    ref = ref_block(c, tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "G=128")
+
+
+def test_token_mode_long_lists_unpipelined(gpu):
+    """Index lists longer than the pipelined 128-head kernel can stage in LDS
+    (more than 15104 ids per token, 256 tokens so nothing is split): the
+    gather kernel with 64-key tiles."""
+    rng = np.random.default_rng(70)
+    T, Hq, S, topk = 256, 128, 20000, 15360
+    q8 = rand_codes(rng, (T, Hq, 576), 2.0)
+    kv8 = rand_codes(rng, (S, 576))
+    idx = np.stack([rng.permutation(S)[:topk] for _ in range(T)]).astype(np.int32)
+    idx[0, :] = -1
+    idx[1, ::3] = -1
+    tl = np.full(T, topk, np.int32)
+    tl[2], tl[3] = 1, 8000
+    sk = (rng.standard_normal(Hq) * 3).astype(np.float32)
+    got = run_token(gpu, q8, kv8, idx, 1 / 24, q_scale=0.9, v_scale=1.5, attn_sink=sk, topk_length=tl)
+    toks = np.array([0, 1, 2, 3, 100, 255])
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, q_scale=0.9, v_scale=1.5, attn_sink=sk,
+                               topk_length=tl, tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "long lists")
+
+
+def test_token_mode_cache_past_2gb(gpu):
+    """A 2.2 GB KV array (3.8M rows of 576 bytes): byte offsets outside the
+    pipelined kernel's 32-bit range send 128-head groups to the gather kernel
+    with 64-bit addressing (4 tokens: lists split over workgroups, merged)."""
+    S, T, Hq, topk = 3_800_000, 4, 128, 1024
+    g = torch.Generator(device="cuda").manual_seed(71)
+    kv = torch.empty((S, 576), dtype=torch.uint8, device="cuda")
+    for r0 in range(0, S, 400_000):
+        r1 = min(S, r0 + 400_000)
+        kv[r0:r1] = torch.randn((r1 - r0, 576), generator=g, device="cuda").to(torch.float8_e4m3fn).view(torch.uint8)
+    rng = np.random.default_rng(71)
+    q8 = rand_codes(rng, (T, Hq, 576), 2.0)
+    idx = np.stack([rng.choice(S, topk, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[:, :4] = [S - 1, S - 2, S - 3000, 3_700_123]          # rows past 2 GB
+    idx[1, 500:600] = -1
+    sk = (rng.standard_normal(Hq) * 3).astype(np.float32)
+    got = gpu.sparse_attn_fwd(dev(q8), kv, dev(idx), sm_scale=1 / 24, mode="token", d_v=512, attn_sink=dev(sk),
+                              k_scale=0.7)
+    used = np.unique(idx[idx >= 0])
+    rows = kv[torch.from_numpy(used.astype(np.int64)).cuda()].cpu().numpy()
+    remap = np.full(idx.shape, -1, np.int64)
+    remap[idx >= 0] = np.searchsorted(used, idx[idx >= 0])
+    ref = OA.sparse_attn_token(q8, rows, remap.astype(np.int32), sm_scale=1 / 24, d_v=512, attn_sink=sk,
+                               k_scale=0.7)
+    del kv
+    torch.cuda.empty_cache()
+    assert_attention_close(got, ref, "2 GB cache")

@@ -14,7 +14,7 @@ import torch
 from oracle import indexer as OI
 from oracle import quantize as OQ
 import workloads as W
-from helpers import bf16_dev, dev, host, scores_margin_ok, workload
+from helpers import bf16_dev, dev, exact_workload_ids, host, scores_margin_ok, workload
 
 pytestmark = pytest.mark.gpu
 PAGE = 128
@@ -115,29 +115,46 @@ def test_decode_batch_exact(gpu):
     assert_ids_equal(got, ref, "decode")
 
 
-def test_invalid_pages_are_ignored(gpu):
-    iq, ik, bt, cu, sl, mq = make_case([2000], [2000], seed=4)
+@pytest.mark.parametrize("q_lens", [[2000], [1]])
+def test_pages_outside_the_cache_hold_no_keys(gpu, q_lens):
+    """Block-table entries outside [0, num_pages) (-1, one past the cache, far
+    past it) name no page: those blocks score -inf against the oracle's rule,
+    in the prefill (2000 queries) and decode (1 query) score kernels."""
+    iq, ik, bt, cu, sl, mq = make_case([2000], q_lens, seed=4 + len(q_lens) + q_lens[0])
+    P = ik.shape[0]
     bt = bt.copy()
-    bt[0, 3] = 10_000_000          # out of range page: block 3 has no keys
-    got = run(gpu, iq, ik, bt, cu, sl, mq, 4)
-    assert not np.any(got[:, 1000:] == 3)
+    bt[0, [3, 7, 11]] = [-1, P, 10_000_000]
+    for topk in (4, 13):       # 16 blocks, 13 with keys: k = 13 leaves no room for the three
+        got = run(gpu, iq, ik, bt, cu, sl, mq, topk)
+        ref = OI.indexer_topk(iq, ik, bt, cu, sl, sm_scale=0.088, topk=topk)
+        assert_ids_equal(got, ref, f"absent pages k={topk}")
+        assert not np.isin(got[:, -1], [3, 7, 11]).any()
+    # k = 15 of 16: all 13 blocks with keys, then the two lowest ids without one
+    got = run(gpu, iq, ik, bt, cu, sl, mq, 15)
+    ref = OI.indexer_topk(iq, ik, bt, cu, sl, sm_scale=0.088, topk=15)
+    assert_ids_equal(got, ref, "absent pages k=15")
+    assert list(got[0, -1]) == [b for b in range(16) if b != 11]
 
 
-def test_prefill_32k_exact_sampled(gpu):
-    """Full-size 32k prefill indexer (exact-mode codes, U(0.1,4) scales)."""
+def test_prefill_32k_exact_full(gpu):
+    """Full-size 32k prefill indexer (exact-mode codes, U(0.1,4) scales): every
+    one of the 4 x 32768 id rows bit-exact against the oracle."""
     wl = workload(3)
-    iq, ik = wl.extra["idx_q8_exact"], wl.extra["idx_k8_exact"]
+    iq, ik, ref = exact_workload_ids(3)
     got = run(gpu, iq, ik, wl.block_table, wl.cu_seqlens_q, wl.seq_lens, wl.max_q_len, wl.topk,
               sm=wl.idx_sm_scale, qs=wl.idx_q_scale, ks=wl.idx_k_scale)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(np.arange(8192, 32768), 48, replace=False))
-    ref = OI.indexer_topk(iq, ik, wl.block_table, wl.cu_seqlens_q, wl.seq_lens, sm_scale=wl.idx_sm_scale,
-                          idx_q_scale=wl.idx_q_scale, idx_k_scale=wl.idx_k_scale, topk=wl.topk, tokens=toks)
-    assert_ids_equal(got[:, toks], ref, "32k sampled")
-    # all rows below 64 blocks take the padding branch
-    for t in (0, 127, 128, 4000, 8191):
-        nb = t // PAGE + 1
-        assert list(got[2, t]) == list(range(nb)) + [-1] * (64 - nb)
+    assert_ids_equal(got, ref, "32k full")
+
+
+def test_decode_64x32k_exact_full(gpu):
+    """Full-size decode indexer: 64 sequences x 32768 tokens, exact-mode codes,
+    all 4 x 64 id rows bit-exact against the oracle."""
+    wl = workload(5)
+    iq, ik, ref = exact_workload_ids(5)
+    got = run(gpu, iq, ik, wl.block_table, wl.cu_seqlens_q, wl.seq_lens, wl.max_q_len, wl.topk,
+              sm=wl.idx_sm_scale, qs=wl.idx_q_scale, ks=wl.idx_k_scale)
+    assert_ids_equal(got, ref, "decode full")
+    assert np.all(np.diff(got, axis=2) > 0)
 
 
 def test_prefill_8k_padding_branch_full(gpu):

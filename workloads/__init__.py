@@ -176,14 +176,29 @@ def block_workload(B: int, seq_len: int, q_len: int, *, seed: int, name: str, Hq
     sl = np.full(B, seq_len, dtype=np.int32)
     extra = {}
     if exact_index:
-        ex_rng = np.random.default_rng([seed, 7])
-        qv = ex_rng.choice(E4M3_EXACT_INTS, size=(T, Hidx, Didx)) * ex_rng.choice([-1.0, 1.0], size=(T, Hidx, Didx))
-        kv = ex_rng.choice(E4M3_EXACT_INTS[E4M3_EXACT_INTS <= 16], size=(P, PAGE, Didx)) * \
-            ex_rng.choice([-1.0, 1.0], size=(P, PAGE, Didx))
-        extra["idx_q8_exact"] = e4m3_codes(qv.astype(np.float32))
-        extra["idx_k8_exact"] = e4m3_codes(kv.astype(np.float32))
+        extra["idx_q8_exact"], extra["idx_k8_exact"] = exact_index_codes(seed, T, Hidx, Didx, P)
     return BlockWorkload(name, q, iq, kc, vc, ik, bt, cu, sl, q_len, topk, sm, 1.0 / math.sqrt(Didx),
                          q_s, k_s, v_s, iq_s, ik_s, sink, extra)
+
+
+def exact_index_codes(seed: int, T: int, Hidx: int, Didx: int, P: int, chunk_pages: int = 1024):
+    """Exact-mode index codes of a block workload: e4m3-exact integers with
+    random signs, |q| <= 64 for the index query ``[T, Hidx, Didx]`` and
+    |k| <= 16 for the index-key cache ``[P, PAGE, Didx]``, drawn from the
+    child stream ``[seed, 7]`` (so they leave the workload's other draws
+    unchanged).  The key cache is drawn in chunks of ``chunk_pages`` pages to
+    bound memory."""
+    ex_rng = np.random.default_rng([seed, 7])
+    qv = ex_rng.choice(E4M3_EXACT_INTS, size=(T, Hidx, Didx)) * ex_rng.choice([-1.0, 1.0], size=(T, Hidx, Didx))
+    iq = e4m3_codes(qv.astype(np.float32))
+    del qv
+    ik = np.empty((P, PAGE, Didx), np.uint8)
+    kvals = E4M3_EXACT_INTS[E4M3_EXACT_INTS <= 16]
+    for p0 in range(0, P, chunk_pages):
+        n = min(chunk_pages, P - p0)
+        kv = ex_rng.choice(kvals, size=(n, PAGE, Didx)) * ex_rng.choice([-1.0, 1.0], size=(n, PAGE, Didx))
+        ik[p0:p0 + n] = e4m3_codes(kv.astype(np.float32))
+    return iq, ik
 
 
 def workload(n: int, small: bool = False):
