@@ -12,7 +12,7 @@ and the decode batch (64 x 32k, top-64 blocks) follow under "extra_workloads"
 Prints ONE JSON line.  ``value`` = algorithmic attention TFLOP/s over the whole
 step, timed over K replays of the step captured as one HIP graph; ``roofline``
 describes the dominant kernel (sparse attention), timed with HIP events on the
-stream it runs on over K eager steps, each after a 512 MiB write that evicts
+stream it runs on over K eager steps, each after a 512 MiB read that evicts
 the 256 MB last-level cache; ``cpu_baseline`` times the CPU oracle on a
 bounded sample of the same workload.
 
@@ -284,7 +284,7 @@ def measure_qknorm_rope_quantize(fts, T: int, hidx: int, reps: int) -> dict:
 def run_workload(n: int, steps: int, warmup: int, producers: bool) -> dict:
     """Times workload n: K graph replays of the whole step (``value``), then K
     eager steps with HIP events around each call (per-kernel times), each
-    eager step after a 512 MiB write that evicts the last-level cache."""
+    eager step after a 512 MiB read that evicts the last-level cache."""
     import torch
     import fp8_top_sparse_amd as fts
     import workloads as W
@@ -419,12 +419,13 @@ def run_workload(n: int, steps: int, warmup: int, producers: bool) -> dict:
     total_ms = start.elapsed_time(end)
 
     # per-kernel times: K eager steps with HIP events on the launch stream,
-    # each after a 512 MiB write (outside the events) that evicts the 256 MB
-    # last-level cache, so every input comes from HBM
-    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    # each after a 512 MiB read (outside the events) that evicts the 256 MB
+    # last-level cache, so every input comes from HBM; a read leaves no dirty
+    # lines whose write-back would land inside the timed step
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     evs = [new_events() for _ in range(steps)]
     for i in range(steps):
-        flush.fill_(float(i))
+        flush.sum()
         step(evs[i])
     torch.cuda.synchronize()
     ms = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in kinds}
@@ -512,7 +513,7 @@ def main():
         "dtype": "fp8_e4m3 (QK) / bf16 (PV)",
         "data": "synthetic",
         "launch": "one captured HIP graph per step, replayed K times; kernels_ms from K eager steps, "
-                  "each after a 512 MiB cache-evicting write",
+                  "each after a 512 MiB cache-evicting read",
     }
     result["config"] = dict(head.pop("config"), parallelism="single GPU")
     result.update(head)
