@@ -60,6 +60,10 @@ _SIGNATURES = {
     "sparse_attn_fwd": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp, _vp,
                          _sz, _vp], ctypes.c_int),
+    "sparse_attn_fwd_noalloc": ([_i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _i32, _i32, _f32, _fp, _fp, _fp, _vp, _vp, _vp, _vp,
+                                 _vp], ctypes.c_int),
+    "sparse_attn_noalloc_scratch_bytes": ([], _sz),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -266,16 +270,16 @@ def indexer_topk(idx_q: torch.Tensor, idx_k: torch.Tensor, block_table: torch.Te
     return out
 
 
-def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, sm_scale: float,
-                    mode: str = "token", v: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
-                    topk_length: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
-                    cu_seqlens_q: Optional[torch.Tensor] = None, seq_lens: Optional[torch.Tensor] = None,
-                    max_q_len: int = 0, q_scale: Optional[float] = None, k_scale: Optional[float] = None,
-                    v_scale: Optional[float] = None, attn_sink: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    stream=None):
-    """Sparse attention forward.  Returns ``(out bf16, max_logits fp32, lse fp32)``.
+def _attention(noalloc: bool, q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, sm_scale: float,
+               mode: str = "token", v: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
+               topk_length: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+               cu_seqlens_q: Optional[torch.Tensor] = None, seq_lens: Optional[torch.Tensor] = None,
+               max_q_len: int = 0, q_scale: Optional[float] = None, k_scale: Optional[float] = None,
+               v_scale: Optional[float] = None, attn_sink: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None):
+    """Argument marshalling shared by sparse_attn_fwd and sparse_attn_fwd_noalloc.
 
     mode "token": q ``[T, Hq, 576]``, k ``[S, 576]`` (V = first d_v=512 columns
     unless ``v [S, 512]`` is given), indices ``[T, topk]`` token ids.
@@ -353,6 +357,13 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
     _check_out(out, "out", torch.bfloat16, (T, Hq, Dv))
     _check_out(max_logits, "max_logits", torch.float32, (T, Hq))
     _check_out(lse, "lse", torch.float32, (T, Hq))
+    args = (m, _ptr(qb), _ptr(kb), _ptr(vb), num_kv, _ptr(idx), topk, _ptr(tl), _ptr(bt), max_blocks, _ptr(cu),
+            _ptr(sl), B, T, int(max_q_len), Hq, Hkv, Hidx, Dqk, Dv, page, float(sm_scale), _scale(q_scale),
+            _scale(k_scale), _scale(v_scale), _ptr(sink), _ptr(out), _ptr(max_logits), _ptr(lse))
+    if noalloc:
+        _same_device("sparse_attn_fwd_noalloc", dev, qb, kb, vb, idx, tl, bt, cu, sl, sink, out, max_logits, lse)
+        _check(lib.sparse_attn_fwd_noalloc(*args, _stream(stream)))
+        return out, max_logits, lse
     need = lib.sparse_attn_workspace_size(m, B, T, int(max_q_len), Hq, Hkv, Hidx, Dv, topk, max_blocks)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -360,12 +371,56 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, 
         raise ValueError("workspace must be contiguous")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _same_device("sparse_attn_fwd", dev, qb, kb, vb, idx, tl, bt, cu, sl, sink, out, max_logits, lse, workspace)
-    _check(lib.sparse_attn_fwd(m, _ptr(qb), _ptr(kb), _ptr(vb), num_kv, _ptr(idx), topk, _ptr(tl), _ptr(bt),
-                               max_blocks, _ptr(cu), _ptr(sl), B, T, int(max_q_len), Hq, Hkv, Hidx, Dqk, Dv,
-                               page, float(sm_scale), _scale(q_scale), _scale(k_scale), _scale(v_scale),
-                               _ptr(sink), _ptr(out), _ptr(max_logits), _ptr(lse), _ptr(workspace), wsz,
-                               _stream(stream)))
+    _check(lib.sparse_attn_fwd(*args, _ptr(workspace), wsz, _stream(stream)))
     return out, max_logits, lse
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, sm_scale: float,
+                    mode: str = "token", v: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
+                    topk_length: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                    cu_seqlens_q: Optional[torch.Tensor] = None, seq_lens: Optional[torch.Tensor] = None,
+                    max_q_len: int = 0, q_scale: Optional[float] = None, k_scale: Optional[float] = None,
+                    v_scale: Optional[float] = None, attn_sink: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Sparse attention forward.  Returns ``(out bf16, max_logits fp32, lse fp32)``.
+
+    mode "token": q ``[T, Hq, 576]``, k ``[S, 576]`` (V = first d_v=512 columns
+    unless ``v [S, 512]`` is given), indices ``[T, topk]`` token ids.
+    mode "block": q ``[T, Hq, 128]``, k/v ``[pages, Hkv, 128, 128]`` paged caches,
+    indices ``[Hidx, T, topk]`` block ids, plus block_table / cu_seqlens_q /
+    seq_lens / max_q_len as for :func:`indexer_topk`.  ``workspace`` (uint8,
+    at least sparse_attn_workspace_size bytes) is allocated when not given.
+    """
+    return _attention(False, q, k, indices, sm_scale=sm_scale, mode=mode, v=v, d_v=d_v, topk_length=topk_length,
+                      block_table=block_table, cu_seqlens_q=cu_seqlens_q, seq_lens=seq_lens, max_q_len=max_q_len,
+                      q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, attn_sink=attn_sink, out=out,
+                      max_logits=max_logits, lse=lse, workspace=workspace, stream=stream)
+
+
+def sparse_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, indices: torch.Tensor, *, sm_scale: float,
+                            mode: str = "token", v: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
+                            topk_length: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                            cu_seqlens_q: Optional[torch.Tensor] = None, seq_lens: Optional[torch.Tensor] = None,
+                            max_q_len: int = 0, q_scale: Optional[float] = None, k_scale: Optional[float] = None,
+                            v_scale: Optional[float] = None, attn_sink: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, max_logits: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None):
+    """:func:`sparse_attn_fwd` on the library's own per-device scratch (no
+    workspace argument, no device allocation inside the library call).  The
+    library allocates nothing; to keep the whole call allocation-free pass
+    ``out``, ``max_logits`` and ``lse``.  Calls needing more scratch than
+    ``sparse_attn_noalloc_scratch_bytes()`` raise ValueError."""
+    return _attention(True, q, k, indices, sm_scale=sm_scale, mode=mode, v=v, d_v=d_v, topk_length=topk_length,
+                      block_table=block_table, cu_seqlens_q=cu_seqlens_q, seq_lens=seq_lens, max_q_len=max_q_len,
+                      q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, attn_sink=attn_sink, out=out,
+                      max_logits=max_logits, lse=lse, stream=stream)
+
+
+def sparse_attn_noalloc_scratch_bytes() -> int:
+    """Bytes of the per-device scratch behind :func:`sparse_attn_fwd_noalloc`."""
+    return int(load().sparse_attn_noalloc_scratch_bytes())
 
 
 def _token_head_view(x: torch.Tensor, name: str):
@@ -536,6 +591,7 @@ def fp8_qknorm_rope_quantize(x: torch.Tensor, norm_weight: torch.Tensor, eps: fl
     return out if write_out else None
 
 
-__all__ = ["fp8_quantize", "fp8_quantize_pair", "indexer_topk", "sparse_attn_fwd", "fp8_cache_store", "fp8_rope_quantize",
+__all__ = ["fp8_quantize", "fp8_quantize_pair", "indexer_topk", "sparse_attn_fwd", "sparse_attn_fwd_noalloc",
+           "sparse_attn_noalloc_scratch_bytes", "fp8_cache_store", "fp8_rope_quantize",
            "fp8_qknorm_rope_quantize", "load", "flatten_to_2d", "EXPORTED",
            "Fp8tsError", "BF16", "FP16", "TOKEN_MODE", "BLOCK_MODE"]

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -389,16 +390,21 @@ size_t sparse_attn_workspace_size(int32_t mode, int32_t batch, int32_t total_q, 
                               head_dim_v, topk, max_blocks);
 }
 
-int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v, int64_t num_kv,
-                    const int32_t *indices, int32_t topk, const int32_t *topk_length,
-                    const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
-                    const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads, int32_t head_dim_qk,
-                    int32_t head_dim_v, int32_t page_size, float sm_scale, const float *q_scale,
-                    const float *k_scale, const float *v_scale, const float *attn_sink, uint16_t *out,
-                    float *max_logits, float *lse, void *workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
-  const char *fn = "sparse_attn_fwd";
+}  // extern "C"
+
+namespace fp8ts {
+
+// Validation and argument set-up shared by the two attention entry points:
+// everything but the workspace.  On success fills `a` (workspace unset) and
+// the workspace size the call needs.
+static int prepare_attention(const char *fn, int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v,
+                             int64_t num_kv, const int32_t *indices, int32_t topk, const int32_t *topk_length,
+                             const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
+                             const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads, int32_t head_dim_qk,
+                             int32_t head_dim_v, int32_t page_size, float sm_scale, const float *q_scale,
+                             const float *k_scale, const float *v_scale, const float *attn_sink, uint16_t *out,
+                             float *max_logits, float *lse, AttnArgs &a, size_t &need) {
   if (mode != FP8TS_TOKEN_MODE && mode != FP8TS_BLOCK_MODE)
     return fail(FP8TS_EINVAL, "%s: mode must be 0 (token) or 1 (block), got %d", fn, mode);
   if (total_q < 0 || num_kv < 0 || topk < 0 || batch < 0 || max_q_len < 0 || max_blocks < 0)
@@ -437,6 +443,7 @@ int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint
     if (topk < 1 || topk > 64) return fail(FP8TS_EUNSUPPORTED, "%s: block mode topk must be in [1, 64] (got %d)", fn, topk);
     if (max_blocks > 4096) return fail(FP8TS_EUNSUPPORTED, "%s: max_blocks %d exceeds 4096", fn, max_blocks);
   }
+  need = 0;
   if (total_q == 0) return FP8TS_OK;
   if (!q || !k || !indices || !out || !max_logits || !lse) return fail(FP8TS_EINVAL, "%s: null tensor pointer", fn);
   if (num_kv == 0) return fail(FP8TS_EINVAL, "%s: empty KV", fn);
@@ -446,16 +453,13 @@ int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint
       return fail(FP8TS_EINVAL, "%s: block mode needs block_table, cu_seqlens_q, seq_lens, batch, max_blocks, max_q_len", fn);
     if (max_q_len > total_q) return fail(FP8TS_EINVAL, "%s: max_q_len %d > total_q %d", fn, max_q_len, total_q);
   }
-  const size_t need = attn_workspace_bytes(mode, batch, total_q, max_q_len, num_q_heads, num_kv_heads,
-                                           num_idx_heads, head_dim_v, topk, max_blocks);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(FP8TS_EINVAL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace ? workspace_bytes : 0);
-  if (need && (uintptr_t)workspace % 256) return fail(FP8TS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  need = attn_workspace_bytes(mode, batch, total_q, max_q_len, num_q_heads, num_kv_heads, num_idx_heads,
+                              head_dim_v, topk, max_blocks);
   const size_t ob = (size_t)total_q * num_q_heads * head_dim_v * 2;
   if (overlaps(out, ob, q, (size_t)total_q * num_q_heads * head_dim_qk))
     return fail(FP8TS_EINVAL, "%s: out overlaps q", fn);
 
-  AttnArgs a{};
+  a = AttnArgs{};
   a.mode = mode;
   a.q = q;
   a.k = k;
@@ -488,8 +492,103 @@ int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint
   a.out = out;
   a.max_logits = max_logits;
   a.lse = lse;
+  return FP8TS_OK;
+}
+
+
+// The library's own scratch for callers that cannot allocate: one copy per
+// device, held until the process ends.  Host code uses the address
+// hipGetSymbolAddress returns on each device, never the symbol itself.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static void *g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch (looked up once per device, with
+// that device current), or null with a message.
+static void *device_scratch(const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(FP8TS_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(FP8TS_EUNSUPPORTED, "%s: device %d is beyond the %d devices the scratch table covers", fn, dev, kMaxDevices);
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (!g_scratch_ptr[dev]) {
+    fail(FP8TS_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+         hipGetErrorString(g_scratch_err[dev]));
+    return nullptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace fp8ts
+
+extern "C" {
+
+int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v, int64_t num_kv,
+                    const int32_t *indices, int32_t topk, const int32_t *topk_length,
+                    const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
+                    const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads, int32_t head_dim_qk,
+                    int32_t head_dim_v, int32_t page_size, float sm_scale, const float *q_scale,
+                    const float *k_scale, const float *v_scale, const float *attn_sink, uint16_t *out,
+                    float *max_logits, float *lse, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const char *fn = "sparse_attn_fwd";
+  AttnArgs a;
+  size_t need = 0;
+  if (int st = prepare_attention(fn, mode, q, k, v, num_kv, indices, topk, topk_length, block_table, max_blocks,
+                                 cu_seqlens_q, seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                 num_idx_heads, head_dim_qk, head_dim_v, page_size, sm_scale, q_scale, k_scale,
+                                 v_scale, attn_sink, out, max_logits, lse, a, need))
+    return st;
+  if (total_q == 0) return FP8TS_OK;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(FP8TS_EINVAL, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace ? workspace_bytes : 0);
+  if (need && (uintptr_t)workspace % 256) return fail(FP8TS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
   a.workspace = workspace;
   return launch_attention(a, stream);
 }
+
+int sparse_attn_fwd_noalloc(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v, int64_t num_kv,
+                            const int32_t *indices, int32_t topk, const int32_t *topk_length,
+                            const int32_t *block_table, int32_t max_blocks, const int32_t *cu_seqlens_q,
+                            const int32_t *seq_lens, int32_t batch, int32_t total_q, int32_t max_q_len,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t num_idx_heads, int32_t head_dim_qk,
+                            int32_t head_dim_v, int32_t page_size, float sm_scale, const float *q_scale,
+                            const float *k_scale, const float *v_scale, const float *attn_sink, uint16_t *out,
+                            float *max_logits, float *lse, hipStream_t stream) {
+  const char *fn = "sparse_attn_fwd_noalloc";
+  AttnArgs a;
+  size_t need = 0;
+  if (int st = prepare_attention(fn, mode, q, k, v, num_kv, indices, topk, topk_length, block_table, max_blocks,
+                                 cu_seqlens_q, seq_lens, batch, total_q, max_q_len, num_q_heads, num_kv_heads,
+                                 num_idx_heads, head_dim_qk, head_dim_v, page_size, sm_scale, q_scale, k_scale,
+                                 v_scale, attn_sink, out, max_logits, lse, a, need))
+    return st;
+  if (total_q == 0) return FP8TS_OK;
+  if (need > kScratchBytes)
+    return fail(FP8TS_EUNSUPPORTED, "%s: the call needs %zu bytes of scratch, more than the library's %zu; "
+                "use sparse_attn_fwd with a workspace", fn, need, kScratchBytes);
+  if (need) {
+    a.workspace = device_scratch(fn);
+    if (!a.workspace) return FP8TS_EHIP;
+  }
+  return launch_attention(a, stream);
+}
+
+size_t sparse_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

@@ -369,6 +369,41 @@ int sparse_attn_fwd(int32_t mode, const uint8_t *q, const uint8_t *k, const uint
                     uint16_t *out, float *max_logits, float *lse, void *workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * sparse_attn_fwd_noalloc - sparse_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Arguments, semantics, outputs and errors
+ * are those of sparse_attn_fwd without the workspace: the split partials and
+ * pre-converted V^T tiles go to a scratch array the library holds in device
+ * memory, one per device, from the first call on that device until the
+ * process ends.  The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine); its only set-up, on the first call on a
+ * device, looks up that device's scratch address.
+ *
+ * Limit: calls whose sparse_attn_workspace_size(...) exceeds
+ * sparse_attn_noalloc_scratch_bytes() (32 MiB) return FP8TS_EUNSUPPORTED and
+ * launch nothing.  Nothing in the scratch has to start at zero (every byte a
+ * call reads was written earlier in the same call).
+ * Concurrency: every call on one device uses that device's one scratch array,
+ * so calls that overlap in time on one device (different streams, or host
+ * threads without ordering) race; calls ordered on one stream do not.
+ * Errors: as sparse_attn_fwd, plus FP8TS_EHIP when the scratch address cannot
+ * be obtained on the current device.
+ */
+int sparse_attn_fwd_noalloc(int32_t mode, const uint8_t *q, const uint8_t *k, const uint8_t *v,
+                            int64_t num_kv, const int32_t *indices, int32_t topk,
+                            const int32_t *topk_length, const int32_t *block_table,
+                            int32_t max_blocks, const int32_t *cu_seqlens_q,
+                            const int32_t *seq_lens, int32_t batch, int32_t total_q,
+                            int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t num_idx_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                            int32_t page_size, float sm_scale, const float *q_scale,
+                            const float *k_scale, const float *v_scale, const float *attn_sink,
+                            uint16_t *out, float *max_logits, float *lse, hipStream_t stream);
+
+/* Bytes of the per-device scratch behind sparse_attn_fwd_noalloc. */
+size_t sparse_attn_noalloc_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif
