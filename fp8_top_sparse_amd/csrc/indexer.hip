@@ -21,7 +21,9 @@
 //    writes the closed form 0 .. nb - 1, -1 ... and nothing is scored.
 //  * select kernel (wave64): one wave per (head, token) row.  The k-th largest
 //    score is found by a bitwise search over order-preserving uint32 keys
-//    (32 steps of compare + ballot + popcount, no LDS); ties at the threshold go to
+//    (compare + ballot + popcount per bit, no LDS; it starts below the bits
+//    the row's smallest and largest keys share and stops once exactly k keys
+//    reach the candidate); ties at the threshold go to
 //    the lower block id; the survivors are written by ordered compaction
 //    (ballot + popcount prefix), which yields ascending ids without a sort.
 //    The designs on the pages rank by pairwise comparison (an O(k^2)
@@ -409,14 +411,35 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     key[e] = id < nb ? order_key(sc[id]) : 0u;
   }
 
-  // largest thr with |{key >= thr}| >= k, i.e. the k-th largest key
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  // largest thr with |{key >= thr}| >= k, i.e. the k-th largest key.  It
+  // lies between the row's smallest and largest keys, so it shares every bit
+  // above the highest bit in which those two differ: the search starts
+  // there.  And once exactly k keys reach a candidate, that candidate already
+  // separates the top k (the k-th and (k+1)-th keys differ), so the search
+  // stops.
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kmax = max(kmax, key[e]);
+    kmin = min(kmin, key[e] ? key[e] : 0xFFFFFFFFu);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+  }
+  const uint32_t diff = kmin ^ kmax;
+  const int top = diff ? 31 - __clz(diff) : -1;
+  uint32_t thr = top >= 31 ? 0u : (kmax >> (top + 1)) << (top + 1);
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(key[e] >= cand));
-    if (cnt >= k) thr = cand;
+    if (cnt >= k) {
+      thr = cand;
+      if (cnt == k) break;
+    }
   }
   int above = 0;
 #pragma unroll
