@@ -486,7 +486,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
 
 // ---------------------------------------------------------------- host side
 constexpr int kDecodeChunk = 32;   // union blocks per tile-decode workgroup
-constexpr int kStreamChunk = 32;   // union blocks per streamed-decode workgroup
+constexpr int kStreamChunk = 64;   // most union blocks per streamed-decode workgroup
+constexpr int kStreamMin = 8;      // fewest union blocks per streamed-decode workgroup
+constexpr int kCUs = 256;          // compute units of an MI355X
 
 struct Plan {
   int kind;   // 0 block prefill (single-buffered), 2 token 128 heads, 3 token 16 heads,
@@ -542,8 +544,15 @@ Plan make_plan(int mode, int batch, int total_q, int max_q_len, int hq, int hkv,
         sg.NL = sg.TT * sg.n_il;
         int sbound = sg.n_il * (sg.TT < max_q_len ? sg.TT : max_q_len) * topk;
         if (sbound > max_blocks) sbound = max_blocks;
-        sg.splits = (sbound + kStreamChunk - 1) / kStreamChunk;
-        if (sg.splits < 1) sg.splits = 1;
+        // one workgroup per CU (each holds 128 KB of LDS), but no fewer
+        // than kStreamMin and no more than kStreamChunk blocks per workgroup
+        const int64_t tiles = (int64_t)batch * hkv * sg.n_tiles;
+        const int64_t want = (kCUs + tiles - 1) / tiles;
+        const int64_t most = (sbound + kStreamMin - 1) / kStreamMin;
+        int64_t sp = want < most ? want : most;
+        const int64_t least = (sbound + kStreamChunk - 1) / kStreamChunk;
+        if (sp < least) sp = least;
+        sg.splits = sp < 1 ? 1 : (int)sp;
         if (block_stream_decode_lds(sg) <= kMaxLds) {
           gr = sg;
           pl.kind = 7;
