@@ -139,6 +139,34 @@ def token_positions(cu_seqlens_q, seq_lens):
     return seq, sl[seq] - (cu[1:] - cu[:-1])[seq] + (np.arange(int(cu[-1])) - start)
 
 
+def timed_copies(pairs, flush, reps: int) -> dict:
+    """A reference for small HBM-bound launches: torch device copies dst <- src
+    of the same input tensors, one launch each as the producer makes, timed
+    the same way (cache-evicting read between repetitions).  Bytes: 2 read +
+    2 written per bf16 element."""
+    import torch
+    nbytes = sum(4 * src.numel() for src, _ in pairs)
+
+    def run():
+        for src, dst in pairs:
+            dst.copy_(src)
+
+    run()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.mean(times))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"launches": len(pairs), "ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def measure_cache_store(fts, wl, block: bool, reps: int) -> dict:
     """fp8_cache_store of the workload's new keys into fresh caches, HBM-bound.
 
@@ -191,8 +219,10 @@ def measure_cache_store(fts, wl, block: bool, reps: int) -> dict:
         times.append(a.elapsed_time(b))
     ms = float(np.mean(times))
     gbps = nbytes / (ms * 1e-3) / 1e9
+    copies = [(x, torch.empty_like(x)) for x, _, _, _ in jobs]
     return {"ms": round(ms, 4), "launches": len(jobs), "bytes": int(nbytes), "GBps": round(gbps, 1),
-            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "device_copy_same_inputs": timed_copies(copies, flush, reps)}
 
 
 def measure_rope_quantize(fts, Q, reps: int) -> dict:
@@ -277,8 +307,10 @@ def measure_qknorm_rope_quantize(fts, T: int, hidx: int, reps: int) -> dict:
         times.append(a.elapsed_time(b))
     ms = float(np.mean(times))
     gbps = nbytes / (ms * 1e-3) / 1e9
+    copies = [(iq, torch.empty_like(iq)), (ik, torch.empty_like(ik))]
     return {"launches": 2, "ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1),
-            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "device_copy_same_inputs": timed_copies(copies, flush, reps)}
 
 
 def run_workload(n: int, steps: int, warmup: int, producers: bool) -> dict:
