@@ -54,11 +54,9 @@ constexpr int kWaveLds = 2 * kPageBytes;
 __device__ __forceinline__ int k_swz(int r) { return ((r & 7) + ((r >> 3) & 1)) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef int v2i_ __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v2i_ lds_v2i;
 
 // 8 e4m3 bytes (keys of one dim) -> the 8 bf16 of a 16x16x32 A operand
-__device__ __forceinline__ v8bf widen8(v2i_ b) {
+__device__ __forceinline__ v8bf widen8(v2i b) {
   const uint32_t lo = (uint32_t)b[0], hi = (uint32_t)b[1];
   const v4i w = {(int)bf16x2_from_e4m3(lo, false), (int)bf16x2_from_e4m3(lo, true),
                  (int)bf16x2_from_e4m3(hi, false), (int)bf16x2_from_e4m3(hi, true)};
@@ -71,7 +69,7 @@ __device__ __forceinline__ v8bf widen8(v2i_ b) {
 // wait for every buffer-to-LDS load in flight before it, including those of
 // the next block that the kernel keeps in flight on purpose.  The outputs are
 // early-clobber: no output may share a register with the address.
-__device__ __forceinline__ void tr_read8x8(const uint8_t *p, v2i_ (&r)[kNdt]) {
+__device__ __forceinline__ void tr_read8x8(const uint8_t *p, v2i (&r)[kNdt]) {
   static_assert(kNdt == 8, "eight dim tiles");
   const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
   asm volatile(
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_kernel(AttnArgs a, Gr
       else __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
       // ---- V^T operands: row tr_row of group g in chunk q is key
       // 32 q + 4 g + r (r < 4) or 32 q + 16 + 4 g + (r - 4)
-      v2i_ vraw[4][kNdt];
+      v2i vraw[4][kNdt];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int key = 32 * q + (tr_row < 4 ? 4 * g + tr_row : 16 + 4 * g + tr_row - 4);
