@@ -94,11 +94,7 @@ def _same(a, b, what):
         assert torch.equal(x, y), f"{what}: {k} differs"
 
 
-@pytest.mark.parametrize("n", [3, 5, 1, 4])
-def test_graph_replay_is_bitexact(gpu, n):
-    """3: GQA prefill with scales and real selection; 5: batched decode with the
-    split-K combine; 1: tiny MLA (16-head kernel, list splits); 4: 128-head MLA."""
-    wl = W.workload(n, small=True)
+def _check_replays(wl):
     step, outs = _path(wl)
     eager = outs()
     step(eager)
@@ -132,6 +128,20 @@ def test_graph_replay_is_bitexact(gpu, n):
         for k in ("out", "ml", "lse"):
             g_out[k].zero_()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [3, 5, 1, 4])
+def test_graph_replay_is_bitexact(gpu, n):
+    """3: GQA prefill with scales and real selection; 5: batched decode with the
+    split-K combine; 1: tiny MLA (16-head kernel, list splits); 4: 128-head MLA."""
+    _check_replays(W.workload(n, small=True))
+
+
+def test_graph_replay_is_bitexact_32k_prefill(gpu):
+    """The 32768-token GQA prefill at full size, the step bench.py replays: its
+    rows see more causal blocks than they select, so the attention runs the
+    16-wave configuration, and the indexer scores and selects."""
+    _check_replays(W.workload(3))
 
 
 def test_producers_graph_replay_is_bitexact(gpu):
