@@ -402,6 +402,10 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
               }
           }
           // ---- row maxima (S units), first-tile references, overflow check
+          // mx: the maximum over this lane's 16 keys of the half.  The running
+          // maximum and the overflow test need no other lane (mraw is
+          // reduced over the row's four lane groups once, after the loop);
+          // only a row taking its reference gathers its row maximum.
           float mx[kCols];
           bool need_start = false;
 #pragma unroll
@@ -410,17 +414,19 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
               m = fmaxf(fmaxf(m, fmaxf(s[kt][c][0], s[kt][c][1])), fmaxf(s[kt][c][2], s[kt][c][3]));
-            mx[c] = group4_max_swap(m);
+            mx[c] = m;
             if (rsel[c]) mraw[c] = fmaxf(mraw[c], mx[c] - negm[c]);
             need_start |= rsel[c] && !started[c];
           }
           if (__any(need_start)) {
-            // rows selecting their first block take this half's maximum as the
-            // reference (half 0 of a selected block always holds a visible key)
+            // rows selecting their first block take this half's row maximum
+            // as the reference (half 0 of a selected block always holds a
+            // visible key)
 #pragma unroll
             for (int c = 0; c < kCols; ++c) {
+              const float row_max = group4_max_swap(mx[c]);   // every lane takes part
               const bool st = rsel[c] && !started[c];
-              const float delta = st ? mx[c] : 0.f;
+              const float delta = st ? row_max : 0.f;
 #pragma unroll
               for (int kt = 0; kt < 4; ++kt) s[kt][c] -= delta;
               mx[c] -= delta;
@@ -495,6 +501,10 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       // PRE: the DMA of tile it + 1 lands before the next barrier
       if constexpr (C::kPre) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
+    // the exact row maxima: the lanes' running maxima over the row's four
+    // lane groups
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) mraw[c] = group4_max_swap(mraw[c]);
     // rare second pass: restart from the exact row maxima seen in the first one
     if (pass == 1 || !__syncthreads_or(overflow)) break;
 #pragma unroll
