@@ -269,7 +269,8 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   // ---------------------------------------------------------------- state
   v4f o[kNdt][kCols];
   float negm[kCols];      // minus the reference maximum (raw dot units); 0 before the first tile
-  float mraw[kCols];      // exact running maximum (raw dot units)
+  float mraw[kCols];      // exact row maximum (raw dot units), set at the end of a pass
+  float msh[kCols];       // this lane's running maximum of S (raw units minus the reference)
   float lsum[kCols];
   bool started[kCols];
 #pragma unroll
@@ -278,6 +279,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
     for (int dt = 0; dt < kNdt; ++dt) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
     negm[c] = 0.f;
     mraw[c] = -INFINITY;
+    msh[c] = -INFINITY;
     lsum[c] = 0.f;
     started[c] = false;
   }
@@ -301,7 +303,6 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   int m_page_v = 0, m_blk_v = 0;
   uint32_t m_word[kCols];
   for (int pass = 0; pass < 2; ++pass) {
-    bool overflow = false;
     if constexpr (C::kPre) {
       if (n_iter > 1) {
         m_page_v = plist[1];
@@ -401,13 +402,13 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
                   if (pos > br.row_p[c]) s[kt][c][i] = -INFINITY;
               }
           }
-          // ---- row maxima (S units), first-tile references, overflow check
-          // mx: the maximum over this lane's 16 keys of the half.  The running
-          // maximum and the overflow test need no other lane (mraw is
-          // reduced over the row's four lane groups once, after the loop);
-          // only a row taking its reference gathers its row maximum.
+          // ---- first-block references.  mx: the maximum over this lane's 16
+          // keys of the half.  The running maximum needs no other lane (the
+          // row's four lane groups are reduced after the key loop, where the
+          // overflow test also runs); only rows taking their reference gather
+          // their row maximum.  A row takes it in half 0 of the first block it
+          // selected, so half 1 never does.
           float mx[kCols];
-          bool need_start = false;
 #pragma unroll
           for (int c = 0; c < kCols; ++c) {
             float m = -INFINITY;
@@ -415,8 +416,11 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
             for (int kt = 0; kt < 4; ++kt)
               m = fmaxf(fmaxf(m, fmaxf(s[kt][c][0], s[kt][c][1])), fmaxf(s[kt][c][2], s[kt][c][3]));
             mx[c] = m;
-            if (rsel[c]) mraw[c] = fmaxf(mraw[c], mx[c] - negm[c]);
-            need_start |= rsel[c] && !started[c];
+          }
+          bool need_start = false;
+          if (h == 0) {
+#pragma unroll
+            for (int c = 0; c < kCols; ++c) need_start |= rsel[c] && !started[c];
           }
           if (__any(need_start)) {
             // rows selecting their first block take this half's row maximum
@@ -436,8 +440,9 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
               cinit[c] = (v4f){cv, cv, cv, cv};
             }
           }
+          // rows that did not select the block hold -inf here (C = -inf)
 #pragma unroll
-          for (int c = 0; c < kCols; ++c) overflow |= mx[c] * ck > kHeadroom;
+          for (int c = 0; c < kCols; ++c) msh[c] = fmaxf(msh[c], mx[c]);
           // ---- probabilities, row sums, bf16 B operands
           v8bf pb[2][kCols];
 #pragma unroll
@@ -501,10 +506,16 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       // PRE: the DMA of tile it + 1 lands before the next barrier
       if constexpr (C::kPre) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
-    // the exact row maxima: the lanes' running maxima over the row's four
-    // lane groups
+    // the exact row maxima (the lanes' running maxima over the row's four
+    // lane groups, back in raw units); a probability past 2^kHeadroom means
+    // the reference was too far below the maximum for fp32
+    bool overflow = false;
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) mraw[c] = group4_max_swap(mraw[c]);
+    for (int c = 0; c < kCols; ++c) {
+      overflow |= msh[c] * ck > kHeadroom;
+      mraw[c] = group4_max_swap(msh[c]) - negm[c];
+      msh[c] = -INFINITY;
+    }
     // rare second pass: restart from the exact row maxima seen in the first one
     if (pass == 1 || !__syncthreads_or(overflow)) break;
 #pragma unroll
