@@ -402,47 +402,41 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
                   if (pos > br.row_p[c]) s[kt][c][i] = -INFINITY;
               }
           }
-          // ---- first-block references.  mx: the maximum over this lane's 16
-          // keys of the half.  The running maximum needs no other lane (the
-          // row's four lane groups are reduced after the key loop, where the
-          // overflow test also runs); only rows taking their reference gather
-          // their row maximum.  A row takes it in half 0 of the first block it
-          // selected, so half 1 never does.
-          float mx[kCols];
+          // ---- running maxima, first-block references.  msh: the lane's
+          // running maximum of S, a chain of 3-input maxima over its 16 keys of
+          // the half (rows that did not select the block hold -inf here, C
+          // being -inf).  It needs no other lane: the row's four lane groups
+          // are reduced after the key loop, where the overflow test also runs.
+          // Only rows taking their reference gather their row maximum; a row
+          // takes it in half 0 of the first block it selected (its running
+          // maximum is then this half's), so half 1 never does.
+          bool need_start = false;
 #pragma unroll
           for (int c = 0; c < kCols; ++c) {
-            float m = -INFINITY;
+            float m = msh[c];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-              m = fmaxf(fmaxf(m, fmaxf(s[kt][c][0], s[kt][c][1])), fmaxf(s[kt][c][2], s[kt][c][3]));
-            mx[c] = m;
-          }
-          bool need_start = false;
-          if (h == 0) {
-#pragma unroll
-            for (int c = 0; c < kCols; ++c) need_start |= rsel[c] && !started[c];
+            for (int kt = 0; kt < 4; ++kt) {
+              m = fmaxf(fmaxf(m, s[kt][c][0]), s[kt][c][1]);
+              m = fmaxf(fmaxf(m, s[kt][c][2]), s[kt][c][3]);
+            }
+            msh[c] = m;
+            if (h == 0) need_start |= rsel[c] && !started[c];
           }
           if (__any(need_start)) {
-            // rows selecting their first block take this half's row maximum
-            // as the reference (half 0 of a selected block always holds a
-            // visible key)
 #pragma unroll
             for (int c = 0; c < kCols; ++c) {
-              const float row_max = group4_max_swap(mx[c]);   // every lane takes part
+              const float row_max = group4_max_swap(msh[c]);   // every lane takes part
               const bool st = rsel[c] && !started[c];
               const float delta = st ? row_max : 0.f;
 #pragma unroll
               for (int kt = 0; kt < 4; ++kt) s[kt][c] -= delta;
-              mx[c] -= delta;
+              msh[c] -= delta;
               negm[c] -= delta;
               started[c] = started[c] || st;
               const float cv = rsel[c] ? negm[c] : -INFINITY;
               cinit[c] = (v4f){cv, cv, cv, cv};
             }
           }
-          // rows that did not select the block hold -inf here (C = -inf)
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) msh[c] = fmaxf(msh[c], mx[c]);
           // ---- probabilities, row sums, bf16 B operands
           v8bf pb[2][kCols];
 #pragma unroll
