@@ -68,7 +68,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
   uint8_t *vt_s = smem + L::K_BYTES;
   int32_t *idx_s = reinterpret_cast<int32_t *>(smem + L::IDX_OFF);
 
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
   const int64_t T = a.total_q;
 
   // ---------------------------------------------------------------- work item
-  int bid = blockIdx.x;
+  int bid = block_index();
   const int split = bid % gr.splits;
   bid /= gr.splits;
 
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
         }
         idx_s[j] = id;
       }
-      n_valid_keys = __syncthreads_count(tid < KT && idx_s[tid < KT ? tid : 0] >= 0);
+      n_valid_keys = wg_count<WAVES>(tid < KT && idx_s[tid < KT ? tid : 0] >= 0);
       for (int ch = tid; ch < KT * (DQK / 16); ch += NT) {
         const int key = ch / (DQK / 16);
         const int part = ch - key * (DQK / 16);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnArgs a, Grid gr) {
     }
   }
   // rare second pass: restart from the exact row maxima seen in the first one
-  if (pass == 1 || !__syncthreads_or(overflow)) break;
+  if (pass == 1 || !wg_or<WAVES>(overflow)) break;
 #pragma unroll
   for (int c = 0; c < COLS; ++c) {
     m_used[c] = m_true[c];
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
   // one workgroup per (token, head) row; thread i owns DV / 128 consecutive dims
   constexpr int VPT = DV / 128;
   static_assert(VPT == 1 || VPT == 4, "combine: 128 or 512 output dims");
-  const int64_t rowidx = blockIdx.x;            // t * hq + h
+  const int64_t rowidx = block_index();            // t * hq + h
   const int h = (int)(rowidx % a.hq);
   const int64_t TH = (int64_t)a.total_q * a.hq;
   const bool has_sink = a.sink != nullptr;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
   float acc[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) acc[j] = 0.f;
-  const int d0 = threadIdx.x * VPT;
+  const int d0 = thread_index() * VPT;
   if (M != -INFINITY) {
     for (int s = 0; s < gr.splits; ++s) {
       const v4f pm = *reinterpret_cast<const v4f *>(gr.part_ml + (s * TH + rowidx) * 4);
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, Grid gr) 
   } else {
     orow[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * scale));
   }
-  if (threadIdx.x == 0) {
+  if (thread_index() == 0) {
     a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
     a.max_logits[rowidx] = mtrue * kLn2;
   }

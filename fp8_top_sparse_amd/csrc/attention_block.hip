@@ -128,11 +128,12 @@ __device__ __forceinline__ void vt_store_unit(uint8_t *vt, int u, const uint32_t
 // (b * max_blocks + j) * hkv + kvh; slots without a valid page are skipped.
 __global__ __launch_bounds__(256) void vt_pages_kernel(AttnArgs a, uint8_t *vt_pages) {
   __shared__ __attribute__((aligned(16))) uint8_t vt_s[kVBytes];
-  const int slot = blockIdx.x;
+  const int slot = block_index();
   const int kvh = slot % a.hkv;
-  const int page = a.block_table[slot / a.hkv];
+  // scalar copy of the workgroup's page: keeps the buffer resource scalar
+  const int page = __builtin_amdgcn_readfirstlane(a.block_table[slot / a.hkv]);
   if (page < 0 || page >= a.num_kv) return;
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   const __amdgpu_buffer_rsrc_t rv = make_tile_rsrc(a.v + ((int64_t)page * a.hkv + kvh) * kPage * kD);
 #pragma unroll
   for (int j = 0; j < kVUnits / 256; ++j) {
@@ -165,13 +166,13 @@ __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::
 void attn_block_kernel(AttnArgs a, Grid gr) {
   constexpr int kThreads = C::kThreads, kCols = C::kCols, kBufs = C::kBufs, kMetaOff = C::kMetaOff;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int col = lane & 15;
 
-  int bid = blockIdx.x;
+  int bid = block_index();
   const int split = bid % gr.splits;
   bid /= gr.splits;
   BlockRows<kCols> br;
@@ -244,11 +245,15 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   // l holds key 16 kt + (l & 15), bytes 32 (l >> 4) + 16 hh; the V^T tile is
   // copied as it stands in the workspace.  16 + 32 wave-sized 1 KB slots.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  // the sequence is workgroup-uniform: read it into a scalar so that the
+  // V^T buffer resource below is scalar too (a resource the compiler sees as
+  // per-lane costs a loop over its distinct values around every load)
+  const int b_s = __builtin_amdgcn_readfirstlane(br.b);
   auto dma_tile = [&](int page, int blk, uint8_t *buf) {
     if (page < 0) return;
     const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.k + ((int64_t)page * a.hkv + kvh_s) * kv_head_stride);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        gr.vt_pages + (((int64_t)br.b * a.max_blocks + blk) * a.hkv + kvh_s) * kVBytes, (short)0, kVBytes,
+        gr.vt_pages + (((int64_t)b_s * a.max_blocks + blk) * a.hkv + kvh_s) * kVBytes, (short)0, kVBytes,
         0x00020000);
     constexpr int kW = kThreads / 64;
     static_assert(16 % kW == 0, "K slots per wave");
@@ -511,7 +516,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       msh[c] = -INFINITY;
     }
     // rare second pass: restart from the exact row maxima seen in the first one
-    if (pass == 1 || !__syncthreads_or(overflow)) break;
+    if (pass == 1 || !wg_or<C::kWaves>(overflow)) break;
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
       started[c] = mraw[c] != -INFINITY;

@@ -88,13 +88,13 @@ void attn_token_kernel(AttnArgs a, Grid gr) {
   constexpr int kCols = 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t *idx_s = reinterpret_cast<int32_t *>(smem + kIdxOff);
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int col = lane & 15;
 
-  int bid = blockIdx.x;
+  int bid = block_index();
   const int split = bid % gr.splits;
   bid /= gr.splits;
   const int hg = bid % gr.n_tiles;
@@ -124,7 +124,7 @@ void attn_token_kernel(AttnArgs a, Grid gr) {
     idx_s[j] = id;
     bad |= id < 0;
   }
-  const bool all_valid = __syncthreads_count(bad) == 0;
+  const bool all_valid = !wg_or<kWaves>(bad);
 
   // ---------------------------------------------------------------- Q operands
   v8i qb[kNkc];
@@ -341,7 +341,7 @@ void attn_token_kernel(AttnArgs a, Grid gr) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
     // rare second pass: restart from the exact row maxima seen in the first one
-    if (pass == 1 || !__syncthreads_or(overflow)) break;
+    if (pass == 1 || !wg_or<kWaves>(overflow)) break;
     started = mraw[0] != -INFINITY;
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {

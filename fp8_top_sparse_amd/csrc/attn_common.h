@@ -136,7 +136,7 @@ template <int NT>
 __device__ __forceinline__ int block_union(const AttnArgs &a, const Grid &gr, int kvh, int cu0, int q_len,
                                            int seq_len, int t0, uint32_t *bits, int32_t *ucount,
                                            int32_t *ulist) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int64_t T = a.total_q;
   uint32_t *ubits = bits + gr.NL * gr.W;
   const int gi_lo = (kvh * gr.G) / gr.gqi;

@@ -20,6 +20,41 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// ---------------------------------------------------------------- ids and workgroup votes
+// Workgroup and thread index (x dimension) read from the registers the
+// hardware loads at wave launch.  blockIdx / threadIdx and the
+// __syncthreads_or/_count votes are device-library functions; the inliner
+// leaves them out of very large kernels (it caps a function's basic-block
+// count), and the result of a call is then taken to differ between lanes:
+// every index derived from the workgroup id lands in vector registers, and a
+// buffer resource built from one is rebuilt in a loop over the lanes' values
+// around each load.
+__device__ __forceinline__ int block_index() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int thread_index() { return (int)__builtin_amdgcn_workitem_id_x(); }
+
+// Number of threads of the workgroup (WAVES waves of 64) whose predicate
+// holds.  Every thread must call it; it is a workgroup barrier, and its
+// result is the same in every thread.
+template <int WAVES>
+__device__ __forceinline__ int wg_count(bool p) {
+  __shared__ int wave_count[WAVES];
+  // the ballot needs every lane active: take it before the lane-0 branch
+  const int n_wave = __builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
+  __syncthreads();   // readers of an earlier vote are done with wave_count
+  if ((thread_index() & 63) == 0) wave_count[thread_index() >> 6] = n_wave;
+  __syncthreads();
+  int n = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) n += wave_count[w];
+  return n;
+}
+
+// Whether the predicate holds in any thread of the workgroup (as wg_count).
+template <int WAVES>
+__device__ __forceinline__ bool wg_or(bool p) {
+  return wg_count<WAVES>(p) != 0;
+}
+
 // ---------------------------------------------------------------- MFMA
 // Operand layout used throughout (16x16 output tiles, wave64):
 //   A (16 x K): lane l holds row (l % 16), K-slice (l / 16)

@@ -73,13 +73,13 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
   const int H = a.num_heads;
   constexpr int ROWS = CT * 16;
   const int TT = ROWS / H;                       // tokens per workgroup tile
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = thread_index() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(thread_index() >> 6);
   const int g = lane >> 4;                       // lane group: K-slice / output row group
   const int col = lane & 15;
 
   // grid: x = split (fastest), then sequence, then tile (heavy tiles first)
-  int bid = blockIdx.x;
+  int bid = block_index();
   const int split = bid % splits;
   bid /= splits;
   const int b = bid % a.batch;
@@ -125,7 +125,10 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(IndexerArgs a, int n
 
   const int64_t T = a.total_q;
   for (int blk = split * 4 + wave; blk < nb_tile; blk += 4 * splits) {
-    const int page = a.block_table[(int64_t)b * a.max_blocks + blk];
+    // the page is wave-uniform: a scalar copy keeps the buffer resource below
+    // scalar (one built from a per-lane value costs a loop over its distinct
+    // values around every load)
+    const int page = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
     float mx[CT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) mx[c] = -INFINITY;
@@ -208,13 +211,13 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
   constexpr int K_PER = kPage * kD / 16 / NT;
   const int H = a.num_heads;
   const int TT = kSRows / H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6, g = lane >> 4, col = lane & 15;
 
   // grid: x = sequence (fastest), then tile (heavy tiles first), then page
   // chunk.  Consecutive workgroups go to the 8 XCDs in turn: with the chunk
   // fastest, every tile's chunk c would land on the same XCD, and only the
   // longest tiles have high chunks.
-  int bid = blockIdx.x;
+  int bid = block_index();
   const int b = bid % a.batch;
   bid /= a.batch;
   const int tile = n_tiles - 1 - bid % n_tiles;
@@ -261,7 +264,11 @@ __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(Inde
     const int page = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks + blk]);
     return (page >= 0 && page < a.num_pages) ? page : -1;
   };
-  auto load = [&](int page) {
+  auto load = [&](int page_in) {
+    // page_in is workgroup-uniform, but the compiler keeps the rotating page
+    // numbers in vector registers: without the scalar copy the resource below
+    // would be rebuilt in a loop over the lanes' values around every load
+    const int page = __builtin_amdgcn_readfirstlane(page_in);
     if (page < 0) return;
     const __amdgpu_buffer_rsrc_t rk = make_tile_rsrc(a.idx_k + (int64_t)page * kPage * kD);
 #pragma unroll
@@ -382,9 +389,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // id; ordered ballot compaction then writes the ids ascending.
 template <int E>
 __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int lane = thread_index() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(thread_index() >> 6);
+  const int64_t row = (int64_t)block_index() * 4 + wave;
   const int64_t T = a.total_q;
   if (row >= (int64_t)a.num_heads * T) return;
   const int h = (int)(row / T);
@@ -469,8 +476,8 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
 // closed form 0 .. nb - 1, then -1, whatever the scores.  One wave per
 // (head, token) row, as in the select kernel, writing the row contiguously.
 __global__ __launch_bounds__(256) void indexer_fill_kernel(IndexerArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = thread_index() & 63;
+  const int64_t row = (int64_t)block_index() * 4 + __builtin_amdgcn_readfirstlane(thread_index() >> 6);
   const int64_t T = a.total_q;
   if (row >= (int64_t)a.num_heads * T) return;
   const int t = (int)(row % T);
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(256) void indexer_fill_kernel(IndexerArgs a) {
 // stay 16-byte aligned): k / 4 threads per row, one store each.
 __global__ __launch_bounds__(256) void indexer_fill4_kernel(IndexerArgs a) {
   const int per = a.topk >> 2;                     // threads per row
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gid = (int64_t)block_index() * 256 + thread_index();
   const int64_t row = gid / per;
   const int64_t T = a.total_q;
   if (row >= (int64_t)a.num_heads * T) return;
