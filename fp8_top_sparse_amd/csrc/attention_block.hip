@@ -277,7 +277,10 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   float mraw[kCols];      // exact row maximum (raw dot units), set at the end of a pass
   float msh[kCols];       // this lane's running maximum of S (raw units minus the reference)
   float lsum[kCols];
-  bool started[kCols];
+  // Per-row flags are kept as wave lane masks (bit l: the row of lane l in
+  // column tile c), so that testing and combining them is scalar work:
+  // startm, rows that took their reference maximum.
+  uint64_t startm[kCols];
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
 #pragma unroll
@@ -286,20 +289,30 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
     mraw[c] = -INFINITY;
     msh[c] = -INFINITY;
     lsum[c] = 0.f;
-    started[c] = false;
+    startm[c] = 0;
   }
   const float ck = a.key_scale_log2;
   const int op_lane = 16 * lane;                       // operand fetch offset of this lane
+  // earliest position among the wave's rows: a half tile whose last key is at
+  // or below it needs no causal mask in any row
+  int wave_pmin = 0x7fffffff;
+#pragma unroll
+  for (int c = 0; c < kCols; ++c)
+    if (br.row_ok[c]) wave_pmin = min(wave_pmin, br.row_p[c]);
+  for (int off = 1; off < 64; off <<= 1) wave_pmin = min(wave_pmin, __shfl_xor(wave_pmin, off, 64));
+  wave_pmin = __builtin_amdgcn_readfirstlane(wave_pmin);
 
-  // metadata of the tile about to be computed, read one tile ahead
+  // metadata of the tile about to be computed, read one tile ahead; t_selm:
+  // lane mask of the rows that selected the tile's block
   int t_blk = 0;
-  bool t_sel[kCols];
+  uint64_t t_selm[kCols];
   auto fetch_meta = [&](int it) {
     t_blk = __builtin_amdgcn_readfirstlane(ulist[lo + it]);
     const bool has_page = __builtin_amdgcn_readfirstlane(plist[it]) >= 0;
 #pragma unroll
     for (int c = 0; c < kCols; ++c)
-      t_sel[c] = has_page && br.row_ok[c] && ((bits[br.row_li[c] * gr.W + (t_blk >> 5)] >> (t_blk & 31)) & 1u);
+      t_selm[c] = __builtin_amdgcn_ballot_w64(
+          has_page && br.row_ok[c] && ((bits[br.row_li[c] * gr.W + (t_blk >> 5)] >> (t_blk & 31)) & 1u));
   };
 
   // PRE: the page and block of tile it + 1 are loaded from LDS during tile
@@ -334,12 +347,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
       const uint8_t *kt_s = smem + (kBufs == 2 ? (it & 1) * kBufBytes : 0);
       const uint8_t *vt_s = kt_s + kKBytes;
       const int blk = t_blk;
-      bool rsel[kCols];
-      bool any_sel = false;
+      uint64_t selm[kCols];
+      uint64_t any_sel = 0;
 #pragma unroll
       for (int c = 0; c < kCols; ++c) {
-        rsel[c] = t_sel[c];
-        any_sel |= rsel[c];
+        selm[c] = t_selm[c];
+        any_sel |= selm[c];
       }
       // stage tile it + 1 (loaded during the previous tile) into the buffer
       // tile it - 1 used, and start loading tile it + 2: this VALU and LDS
@@ -362,12 +375,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
         store_tile(plist[it + 1], smem + ((it + 1) & 1) * kBufBytes);
         if (it + 2 < n_iter) load_tile(plist[it + 2]);
       }
-      if (__any(any_sel)) {
+      if (any_sel) {
         const int key_base = blk * kPage;
         v4f cinit[kCols];
 #pragma unroll
         for (int c = 0; c < kCols; ++c) {
-          const float cv = rsel[c] ? negm[c] : -INFINITY;
+          const float cv = __builtin_amdgcn_inverse_ballot_w64(selm[c]) ? negm[c] : -INFINITY;
           cinit[c] = (v4f){cv, cv, cv, cv};
         }
 #pragma unroll
@@ -391,12 +404,9 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           sched_mfma_then_reads<2, kCols, 2>();
           sched_mfma_then_reads<2, kCols, 0>();
           __builtin_amdgcn_s_setprio(0);
-          // ---- causal mask, only where some row of the wave needs one
+          // ---- causal mask, only where some row of the wave may need one
           const int kpos0 = key_base + 64 * h;
-          bool part = false;
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) part |= rsel[c] && br.row_p[c] < kpos0 + 63;
-          if (__any(part)) {
+          if (kpos0 + 63 > wave_pmin) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -415,7 +425,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           // Only rows taking their reference gather their row maximum; a row
           // takes it in half 0 of the first block it selected (its running
           // maximum is then this half's), so half 1 never does.
-          bool need_start = false;
+          uint64_t need_start = 0;
 #pragma unroll
           for (int c = 0; c < kCols; ++c) {
             float m = msh[c];
@@ -425,20 +435,20 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
               m = fmaxf(fmaxf(m, s[kt][c][2]), s[kt][c][3]);
             }
             msh[c] = m;
-            if (h == 0) need_start |= rsel[c] && !started[c];
+            if (h == 0) need_start |= selm[c] & ~startm[c];
           }
-          if (__any(need_start)) {
+          if (need_start) {
 #pragma unroll
             for (int c = 0; c < kCols; ++c) {
               const float row_max = group4_max_swap(msh[c]);   // every lane takes part
-              const bool st = rsel[c] && !started[c];
+              const bool st = __builtin_amdgcn_inverse_ballot_w64(selm[c] & ~startm[c]);
               const float delta = st ? row_max : 0.f;
 #pragma unroll
               for (int kt = 0; kt < 4; ++kt) s[kt][c] -= delta;
               msh[c] -= delta;
               negm[c] -= delta;
-              started[c] = started[c] || st;
-              const float cv = rsel[c] ? negm[c] : -INFINITY;
+              startm[c] |= selm[c];
+              const float cv = __builtin_amdgcn_inverse_ballot_w64(selm[c]) ? negm[c] : -INFINITY;
               cinit[c] = (v4f){cv, cv, cv, cv};
             }
           }
@@ -447,15 +457,13 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
 #pragma unroll
           for (int c = 0; c < kCols; ++c) {
             float p[4][4];
-            float ls = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 p[kt][i] = __builtin_amdgcn_exp2f(s[kt][c][i] * ck);
-                ls += p[kt][i];
+                lsum[c] += p[kt][i];
               }
-            lsum[c] += ls;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
               v8bf v;
@@ -492,7 +500,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           t_blk = n_blk;
 #pragma unroll
           for (int c = 0; c < kCols; ++c)
-            t_sel[c] = n_page >= 0 && br.row_ok[c] && ((m_word[c] >> (n_blk & 31)) & 1u);
+            t_selm[c] = __builtin_amdgcn_ballot_w64(n_page >= 0 && br.row_ok[c] && ((m_word[c] >> (n_blk & 31)) & 1u));
         } else {
           fetch_meta(it + 1);
         }
@@ -519,8 +527,8 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
     if (pass == 1 || !wg_or<C::kWaves>(overflow)) break;
 #pragma unroll
     for (int c = 0; c < kCols; ++c) {
-      started[c] = mraw[c] != -INFINITY;
-      negm[c] = started[c] ? -mraw[c] : 0.f;
+      startm[c] = __builtin_amdgcn_ballot_w64(mraw[c] != -INFINITY);
+      negm[c] = mraw[c] != -INFINITY ? -mraw[c] : 0.f;
       lsum[c] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < kNdt; ++dt) o[dt][c] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -530,7 +538,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
   float m_ref[kCols], m_true[kCols];
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
-    m_ref[c] = started[c] ? -negm[c] * ck : -INFINITY;
+    m_ref[c] = __builtin_amdgcn_inverse_ballot_w64(startm[c]) ? -negm[c] * ck : -INFINITY;
     m_true[c] = mraw[c] * ck;
   }
   attn_epilogue<kCols, kNdt>(a, gr, split, g, br.row_ok, br.row_t, br.row_h, o, m_ref, m_true, lsum);
