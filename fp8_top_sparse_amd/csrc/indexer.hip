@@ -200,8 +200,10 @@ constexpr int kFlush = 16;
 constexpr int kScPitch = kFlush + 1;          // floats per row of the score buffer
 // pages per workgroup: a tile's causal page range is split into chunks of
 // kSChunk pages, so the grid holds many similar workgroups instead of one
-// per tile (a 32k prompt would otherwise give 384 workgroups of 65..256 pages)
-constexpr int kSChunk = 32;
+// per tile (a 32k prompt would otherwise give 384 workgroups of 65..256
+// pages).  32k prompt: 16 pages 328 us, 32 pages 332 us, 64 pages 350 us
+// for score + select.
+constexpr int kSChunk = 16;
 
 __global__ __launch_bounds__(kSWaves * 64) void indexer_score_shared_kernel(IndexerArgs a, int n_tiles,
                                                                               int n_chunks) {

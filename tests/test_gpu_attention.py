@@ -360,14 +360,18 @@ def test_block_rows_with_no_blocks(gpu):
     assert np.all(out[100:110] == 0) and np.all(np.isneginf(lse[100:110]))
 
 
-def test_block_prefill_late_large_logits(gpu):
+@pytest.mark.parametrize("topk", [7, 8])
+def test_block_prefill_late_large_logits(gpu, topk):
     """Rows whose first blocks carry tiny logits and a later block logits far
     above them (beyond what fp32 can hold relative to the first reference):
     the kernel must rescan with the exact row maxima.  The late block's keys
     have one non-zero coordinate, so its dots are single exact products: the
     fp8 MFMA accumulates with ~16 bits relative to the largest addend, which
-    would otherwise blur logits in the hundreds by more than the lse bound."""
-    c = block_case([900], [900], seed=17, topk=7)
+    would otherwise blur logits in the hundreds by more than the lse bound.
+    top-7 leaves the last rows with more causal blocks than they select (the
+    16-row-wave kernel); top-8 covers every row's blocks (the 32-row-wave
+    kernel)."""
+    c = block_case([900], [900], seed=17, topk=topk)
     rng = np.random.default_rng(17)
     kc = c["kc"].copy()
     bt = c["bt"][0]
@@ -376,8 +380,8 @@ def test_block_prefill_late_large_logits(gpu):
     kc[bt[4], :, :, 0] = W.e4m3_codes(rng.uniform(256, 448, kc.shape[1:3]).astype(np.float32))
     c["kc"] = kc
     nb = np.arange(900) // PAGE + 1
-    ids = np.where(np.arange(7)[None, :] < nb[:, None], np.arange(7)[None, :], -1).astype(np.int32)
-    c["ids"] = np.broadcast_to(ids[None], (4, 900, 7)).copy()
+    ids = np.where(np.arange(topk)[None, :] < nb[:, None], np.arange(topk)[None, :], -1).astype(np.int32)
+    c["ids"] = np.broadcast_to(ids[None], (4, 900, topk)).copy()
     got = run_block(gpu, c)
     ref = ref_block(c)
     ml = ref[2]
