@@ -391,8 +391,12 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
           // when both waves of a SIMD are ready, the one feeding the matrix
           // core goes first and the other's softmax VALU fills its gaps.  The
           // priority changes also keep the exps out of the PV stream
-          // (8k prefill: 263.7 us against 271.2 us, four paired runs)
-          __builtin_amdgcn_s_setprio(1);
+          // (8k prefill: 263.7 us against 271.2 us, four paired runs).  With
+          // four 16-row waves per SIMD they no longer help (32k: 2.675 ms
+          // without against 2.703 ms with, eight paired runs), so that
+          // configuration leaves every wave at the base priority.
+          constexpr int kMfmaPrio = C::kWaves == 16 ? 0 : 1;
+          __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             const v8i ka = lds_read32x2(kt_s + op_lane + 1024 * (2 * (4 * h + kt)));
@@ -476,7 +480,7 @@ void attn_block_kernel(AttnArgs a, Grid gr) {
             }
           }
           // ---- O^T += V^T P^T
-          __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
 #pragma unroll
