@@ -38,6 +38,7 @@ FILE_FLAGS = {
     "attention.hip": NO_NAN,
     "attention_block.hip": NO_NAN,
     "attention_token.hip": NO_NAN,
+    "attention_latent.hip": NO_NAN,
     # MFMA results in VGPRs: the maxima read them with VALU, which cannot read
     # AGPRs without a copy
     "indexer.hip": NO_NAN + ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],

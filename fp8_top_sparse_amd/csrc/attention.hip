@@ -662,6 +662,10 @@ int launch_attention(const AttnArgs &a, hipStream_t stream) {
       break;
     case 7: st = launch_block_stream_decode(a, pl.gr, pl.nblocks, stream); break;
     case 6:
+      if (token_latent_fits(a, pl.gr.splits)) {
+        st = launch_token_latent(a, pl.gr, pl.nblocks, stream);
+        break;
+      }
       if (token_mla_fits(a)) {
         st = launch_token_mla(a, pl.gr, pl.nblocks, stream);
         break;

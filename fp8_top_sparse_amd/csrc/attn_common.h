@@ -253,5 +253,11 @@ size_t token_mla_lds(int topk, int splits);
 int token_mla_rows();
 bool token_mla_fits(const AttnArgs &a);
 int launch_token_mla(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
+// Token-mode MLA kernel for the latent layout, V = the leading 512 bytes of
+// each K row (attention_latent.hip): only K is staged, and PV runs on e4m3
+// MFMA with P as a hi + lo pair of e4m3 codes.
+size_t token_latent_lds(int topk, int splits);
+bool token_latent_fits(const AttnArgs &a, int splits);
+int launch_token_latent(const AttnArgs &a, const Grid &gr, int64_t nblocks, hipStream_t stream);
 
 }  // namespace fp8ts
