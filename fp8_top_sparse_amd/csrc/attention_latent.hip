@@ -52,6 +52,11 @@ constexpr int kKbStride = 8 * 1024 + 128;        // 128 B mod 256 between neighb
 constexpr int kMain = kNkb * kKbStride;
 constexpr int kTileBytes = kMain + kNkb * 1024;
 constexpr int kIdxOff = 2 * kTileBytes;          // the split's index list (int32)
+// Output staging at the end (over the tile buffers): 16 bf16 rows of 1 KB per
+// wave; the 32-byte pitch step puts the 16 rows of each 8-byte write on
+// different banks.
+constexpr int kOutPitch = kDv * 2 + 32;
+static_assert(kWaves * 16 * kOutPitch <= 2 * kTileBytes, "output staging fits the tile buffers");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -124,31 +129,15 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
   const int lo = min(list_len, split * chunk);
   const int hi = min(list_len, lo + chunk);
   const int n_iter = (hi - lo + kKT - 1) / kKT;
-  // ids outside [0, num_kv) and the positions past the list end become -1
-  bool bad = false;
-  for (int j = tid; j < n_iter * kKT; j += kThreads) {
+  // a list entry: ids outside [0, num_kv) and positions past the list end are -1
+  auto list_id = [&](int j) {
     int id = -1;
     if (lo + j < hi) {
       id = a.indices[(int64_t)tok * a.topk + lo + j];
       if (id < 0 || id >= a.num_kv) id = -1;
     }
-    idx_s[j] = id;
-    bad |= id < 0;
-  }
-  const bool all_valid = !wg_or<kWaves>(bad);
-
-  // ---------------------------------------------------------------- Q operands
-  v8i qb[kNkc];
-  long qt[2];
-  {
-    const uint8_t *qrow = a.q + ((int64_t)tok * a.hq + (row_ok[0] ? row_h[0] : 0)) * kDqk;
-#pragma unroll
-    for (int kc = 0; kc < kNkc; ++kc)
-      qb[kc] = row_ok[0] ? gload32(qrow + 128 * kc + 32 * g) : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
-      qt[mm] = row_ok[0] ? *reinterpret_cast<const long *>(qrow + 512 + 32 * mm + 8 * g) : 0;
-  }
+    return id;
+  };
 
   // ---------------------------------------------------------------- staging
   // Wave w moves key block w of a tile: its 8 main operands and its tail, the
@@ -161,8 +150,7 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
   // wave's key block (slot 8 is the tail).  The parts are issued at three
   // points of the previous tile, so that the eight waves' row gathers do not
   // all queue behind the barrier at once.
-  auto dma_part = [&](int it, uint8_t *tb, int part) {
-    const int id = idx_s[it * kKT + 16 * wave_s + col];
+  auto dma_part = [&](int id, uint8_t *tb, int part) {
     uint8_t *blk = tb + kKbStride * wave_s;
     // the uniform part of each byte offset goes in soffset (an instruction
     // offset would move the LDS destination as well)
@@ -177,6 +165,37 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
                                                     512, 0, 0);
     }
   };
+  auto staged_id = [&](int it) { return idx_s[it * kKT + 16 * wave_s + col]; };
+
+  // the first tile's loads (ids read from global memory here) and the Q
+  // operands are in flight while the list is staged
+  if (n_iter > 0) {
+    const int id0 = list_id(16 * wave_s + col);
+    dma_part(id0, smem, 0);
+    dma_part(id0, smem, 1);
+    dma_part(id0, smem, 2);
+  }
+
+  // ---------------------------------------------------------------- Q operands
+  v8i qb[kNkc];
+  long qt[2];
+  {
+    const uint8_t *qrow = a.q + ((int64_t)tok * a.hq + (row_ok[0] ? row_h[0] : 0)) * kDqk;
+#pragma unroll
+    for (int kc = 0; kc < kNkc; ++kc)
+      qb[kc] = row_ok[0] ? gload32(qrow + 128 * kc + 32 * g) : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+      qt[mm] = row_ok[0] ? *reinterpret_cast<const long *>(qrow + 512 + 32 * mm + 8 * g) : 0;
+  }
+
+  bool bad = false;
+  for (int j = tid; j < n_iter * kKT; j += kThreads) {
+    const int id = list_id(j);
+    idx_s[j] = id;
+    bad |= id < 0;
+  }
+  const bool all_valid = !wg_or<kWaves>(bad);
 
   // ---------------------------------------------------------------- state
   v4f o[kNdt][kCols];
@@ -201,10 +220,11 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
 
   for (int pass = 0; pass < 2; ++pass) {
     bool overflow = false;
-    if (n_iter > 0) {
-      dma_part(0, smem, 0);
-      dma_part(0, smem, 1);
-      dma_part(0, smem, 2);
+    if (pass == 1 && n_iter > 0) {
+      const int id0 = staged_id(0);
+      dma_part(id0, smem, 0);
+      dma_part(id0, smem, 1);
+      dma_part(id0, smem, 2);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
@@ -215,7 +235,8 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
       const uint8_t *tb = smem + (it & 1) * kTileBytes;
       const bool next = it + 1 < n_iter;
       uint8_t *nb = smem + ((it + 1) & 1) * kTileBytes;
-      if (next) dma_part(it + 1, nb, 0);
+      const int nid = next ? staged_id(it + 1) : -1;
+      if (next) dma_part(nid, nb, 0);
       v4f cinit[kCols];
 #pragma unroll
       for (int c = 0; c < kCols; ++c) cinit[c] = (v4f){negm[c], negm[c], negm[c], negm[c]};
@@ -276,7 +297,7 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
           mx[c] = group4_max_swap(m);
           mraw[c] = fmaxf(mraw[c], mx[c] - negm[c]);
         }
-        if (h == 0 && next) dma_part(it + 1, nb, 1);
+        if (h == 0 && next) dma_part(nid, nb, 1);
         if (!started) {
           // uniform: every row sees the same keys, so all rows have a finite
           // maximum on the same half tile
@@ -331,7 +352,7 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
       }
       // ---- O^T += V^T (hi + lo)^T: the lo product of tile dt - 1 follows the
       // hi product of tile dt, and the operand reads run one tile ahead
-      if (next) dma_part(it + 1, nb, 2);
+      if (next) dma_part(nid, nb, 2);
       const uint8_t *tr = tb + tr_lane;
       v8i va_prev, va_cur = vt_operand(tr, 0);
 #pragma unroll
@@ -379,7 +400,46 @@ void attn_latent_kernel(AttnArgs a, Grid gr) {
     m_ref[c] = started ? -negm[c] * ck : -INFINITY;
     m_true[c] = mraw[c] * ck;
   }
-  attn_epilogue<kCols, kNdt>(a, gr, split, g, row_ok, row_t, row_h, o, m_ref, m_true, lsum);
+  if (gr.splits > 1) {
+    attn_epilogue<kCols, kNdt>(a, gr, split, g, row_ok, row_t, row_h, o, m_ref, m_true, lsum);
+    return;
+  }
+  // Final outputs: the wave's 16 bf16 rows go through LDS (the tile buffers
+  // are free once every wave has left the loop), so that each store writes
+  // one contiguous 1 KB row instead of 8 bytes of each of 16 rows.
+  const float l_tot = group4_sum(lsum[0]);
+  const int64_t rowidx = (int64_t)tok * a.hq + row_h[0];
+  const bool has_sink = a.sink != nullptr;
+  const float zs = has_sink && row_ok[0] ? a.sink_scale_log2 * a.sink[row_h[0]] : -INFINITY;
+  const float M = fmaxf(m_ref[0], zs);
+  float Lt = 0.f, fo = 0.f;
+  if (M != -INFINITY) {
+    const float wk = m_ref[0] == -INFINITY ? 0.f : exp2f(m_ref[0] - M);
+    Lt = l_tot * wk + (has_sink ? exp2f(zs - M) : 0.f);
+    fo = Lt > 0.f ? wk * a.v_scale / Lt : 0.f;
+  }
+  if (g == 0 && row_ok[0]) {
+    a.lse[rowidx] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+    a.max_logits[rowidx] = m_true[0] * kLn2;
+  }
+  __syncthreads();
+  uint8_t *ob = smem + wave * 16 * kOutPitch;
+#pragma unroll
+  for (int dt = 0; dt < kNdt; ++dt) {
+    const v4f x = o[dt][0] * fo;
+    *reinterpret_cast<uint2 *>(ob + col * kOutPitch + 32 * dt + 8 * g) =
+        make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  }
+  // the wave reads back only what it wrote: its own LDS writes are visible
+  // to it once they have completed
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  const int h0 = hg * kRowsPerWg + wave * 16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const v4i v = *reinterpret_cast<const v4i *>(ob + r * kOutPitch + 16 * lane);
+    if (h0 + r < a.hq)
+      *reinterpret_cast<v4i *>(a.out + ((int64_t)tok * a.hq + h0 + r) * kDv + 8 * lane) = v;
+  }
 }
 
 }  // namespace
