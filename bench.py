@@ -76,7 +76,7 @@ TRAFFIC_SUMMARY = {2: "profiles/attn_block_prefill__gqa_prefill_8192.md",
 # the source file of the attention kernel that dominates each workload's step
 KERNEL_SOURCE = {2: "fp8_top_sparse_amd/csrc/attention_block.hip",
                  3: "fp8_top_sparse_amd/csrc/attention_block.hip",
-                 4: "fp8_top_sparse_amd/csrc/attention_token.hip",
+                 4: "fp8_top_sparse_amd/csrc/attention_latent.hip",
                  5: "fp8_top_sparse_amd/csrc/attention_decode.hip"}
 
 

@@ -217,6 +217,36 @@ def test_single_key_gives_v_bitwise(gpu, Hq):
         assert np.allclose(lse[t], z, rtol=0, atol=1e-3) and np.allclose(ml[t], z, rtol=0, atol=1e-3)
 
 
+@pytest.mark.parametrize("pos", [0, 70, 130, 255])
+def test_latent_rows_single_key_in_any_tile_half_bitwise(gpu, pos):
+    # 128 q heads, V = the leading 512 bytes of each K row: the kernel scores
+    # 64-key halves of 128-key tiles, each half with its own P exponent, and
+    # splits P into two e4m3 codes; one valid entry in either half of the
+    # first or a later tile still gives V exactly
+    q8, kv8, _, _ = token_case(2, 128, 600, 4, seed=21, sink=False)
+    idx = np.full((2, 256), -1, np.int32)
+    idx[0, pos], idx[1, pos] = 11, 599
+    out, ml, lse = (host(x) for x in run_token(gpu, q8, kv8, idx, 1 / 24, v_scale=0.5))
+    for t, j in enumerate([11, 599]):
+        v = TAB[kv8[j, :512]] * 0.5
+        expect = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(out[t], np.broadcast_to(expect, out[t].shape))
+        z = (TAB[q8[t]] @ TAB[kv8[j]]) / 24
+        assert np.allclose(lse[t], z, rtol=0, atol=1e-3) and np.allclose(ml[t], z, rtol=0, atol=1e-3)
+
+
+def test_latent_rows_and_separate_v_match_the_oracle(gpu):
+    # the same inputs through the latent-row kernel (no V argument) and the
+    # separate-V kernel; 1000 entries leave a last tile of 64 + 40 keys
+    q8, kv8, idx, sk = token_case(6, 128, 4096, 1000, seed=22)
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, attn_sink=sk)
+    a = run_token(gpu, q8, kv8, idx, 1 / 24, attn_sink=sk)
+    b = gpu.sparse_attn_fwd(dev(q8), dev(kv8), dev(idx), sm_scale=1 / 24, mode="token",
+                            v=dev(kv8[:, :512].copy()), attn_sink=dev(sk))
+    assert_attention_close(a, ref, "latent rows")
+    assert_attention_close(b, ref, "separate v")
+
+
 @pytest.mark.parametrize("Hq", [16, 128])
 def test_scale_invariants_bitwise(gpu, Hq):
     q8, kv8, idx, sk = token_case(4, Hq, 2000, 130, seed=8)
