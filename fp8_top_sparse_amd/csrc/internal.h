@@ -36,6 +36,23 @@ int launch_cache_store(const StoreArgs &a, int dtype, bool has_scale, float scal
                        hipStream_t stream);
 
 // ---- RoPE + quantize
+// Division by an invariant 32-bit integer as a multiply-high and two shifts
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, section 4): exact for every 32-bit n.
+struct FastDiv {
+  uint32_t m;
+  int32_t s1, s2;
+};
+inline FastDiv make_fastdiv(uint32_t d) {   // d >= 1
+  int l = 0;
+  while ((1ull << l) < d) ++l;              // ceil(log2 d)
+  FastDiv f;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.s1 = l > 0 ? 1 : 0;
+  f.s2 = l > 0 ? l - 1 : 0;
+  return f;
+}
+
 struct RopeArgs {
   const uint16_t *x_nope, *x_pe;     // [N, heads, nope] / [N, heads or 1, rope]
   int64_t nope_ts, nope_hs, pe_ts, pe_hs;  // strides in elements (pe_hs 0: shared rope head)
@@ -46,6 +63,8 @@ struct RopeArgs {
   int64_t num_tokens, max_position;
   int32_t heads, nope, rope;
   bool neox;
+  FastDiv div_nope, div_rope, div_heads;   // by nope / 8, rope / 8, heads (set by the launcher)
+  int32_t rows_per_wg;                     // (set by the launcher)
 };
 int launch_rope_quantize(const RopeArgs &a, int dtype, bool has_scale, float scale_inv,
                          hipStream_t stream);

@@ -362,23 +362,34 @@ __device__ __forceinline__ v2u encode8(const float *f, float s) {
   return (v2u){o[0], o[1]};
 }
 
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv &f) {
+  const uint32_t t = __umulhi(n, f.m);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 template <int DT, bool HAS_SCALE, bool NEOX>
 __global__ __launch_bounds__(256) void rope_quantize_kernel(RopeArgs a, float s) {
   typedef float v4f __attribute__((ext_vector_type(4)));
-  // Chunk index space: first every no-rope chunk (rows x c1), then every rope
-  // chunk (rows x c2), so a wave runs one of the two paths (a 576-wide row has
-  // 64 + 8 chunks; mixing them in one wave would pay for both).
+  // Workgroup w takes rows [w R, w R + R) (row = token x head).  Its chunk
+  // index space holds first the no-rope chunks of its rows (R x c1), then
+  // their rope chunks (R x c2), so a wave runs one of the two paths (a
+  // 576-wide row has 64 + 8 chunks; mixing them in one wave would pay for
+  // both), and every workgroup carries its share of the rope chunks, whose
+  // position and cos/sin loads then overlap other workgroups' streaming
+  // instead of forming the tail of the grid.
   const uint32_t c1 = (uint32_t)a.nope / 8;
   const uint32_t c2 = (uint32_t)a.rope / 8;
   const uint32_t rows = (uint32_t)a.num_tokens * (uint32_t)a.heads;
-  const uint32_t total_a = rows * c1;
-  const uint32_t total = total_a + rows * c2;
+  const uint32_t r0 = blockIdx.x * (uint32_t)a.rows_per_wg;
+  const uint32_t nr = min((uint32_t)a.rows_per_wg, rows - r0);
+  const uint32_t total_a = nr * c1;
+  const uint32_t total = total_a + nr * c2;
   const uint32_t half = (uint32_t)a.rope / 2;
-  const uint32_t stride = gridDim.x * blockDim.x;
+  const uint32_t stride = blockDim.x;
   // Two chunks per thread.  Source loads (and the rotate-half partner) do not
   // depend on the position, so they are issued first; only the cos/sin rows
   // wait for it.
-  for (uint32_t g0 = blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += 2 * stride) {
+  for (uint32_t g0 = threadIdx.x; g0 < total; g0 += 2 * stride) {
     bool live[2], rope[2];
     uint32_t n[2], j0[2];
     uint8_t *dst[2];
@@ -390,9 +401,9 @@ __global__ __launch_bounds__(256) void rope_quantize_kernel(RopeArgs a, float s)
       rope[k] = g >= total_a;
       const uint32_t gi = rope[k] ? g - total_a : g;
       const uint32_t cw = rope[k] ? c2 : c1;
-      const uint32_t r = gi / cw;
-      const uint32_t c = gi - r * cw;
-      n[k] = r / (uint32_t)a.heads;
+      const uint32_t r = r0 + fastdiv(gi, rope[k] ? a.div_rope : a.div_nope);
+      const uint32_t c = gi - (r - r0) * cw;
+      n[k] = fastdiv(r, a.div_heads);
       const uint32_t h = r - n[k] * (uint32_t)a.heads;
       dst[k] = a.out + (int64_t)n[k] * a.out_ts + (int64_t)h * a.out_hs + (rope[k] ? a.nope : 0) + c * 8;
       j0[k] = c * 8;
@@ -449,11 +460,15 @@ __global__ __launch_bounds__(256) void rope_quantize_kernel(RopeArgs a, float s)
 }
 
 template <int DT, bool HAS_SCALE>
-int launch_rope_typed(const RopeArgs &a, float s, hipStream_t stream) {
-  const int64_t total = a.num_tokens * a.heads * ((a.nope + a.rope) / 8);
-  int64_t blocks = (total + 511) / 512;      // two chunks per thread
-  if (blocks > 65536) blocks = 65536;
-  if (blocks < 1) blocks = 1;
+int launch_rope_typed(const RopeArgs &args, float s, hipStream_t stream) {
+  RopeArgs a = args;
+  a.div_nope = make_fastdiv(a.nope >= 8 ? (uint32_t)a.nope / 8 : 1u);
+  a.div_rope = make_fastdiv((uint32_t)a.rope / 8);
+  a.div_heads = make_fastdiv((uint32_t)a.heads);
+  // about 2048 chunks (eight per thread) per workgroup
+  const int64_t rows = a.num_tokens * a.heads;
+  a.rows_per_wg = (int32_t)std::max<int64_t>(1, 2048 / ((a.nope + a.rope) / 8));
+  const int64_t blocks = (rows + a.rows_per_wg - 1) / a.rows_per_wg;
   if (a.neox) {
     hipLaunchKernelGGL((rope_quantize_kernel<DT, HAS_SCALE, true>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a, s);
