@@ -393,11 +393,12 @@ template <int E>
 __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
   const int lane = thread_index() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(thread_index() >> 6);
-  const int64_t row = (int64_t)block_index() * 4 + wave;
+  // grid: x = groups of four tokens (one wave each), y = index head; no
+  // division on the scalar unit, which the search below keeps busy
+  const int h = (int)__builtin_amdgcn_workgroup_id_y();
+  const int t = block_index() * 4 + wave;
   const int64_t T = a.total_q;
-  if (row >= (int64_t)a.num_heads * T) return;
-  const int h = (int)(row / T);
-  const int t = (int)(row % T);
+  if (t >= T) return;
   const int k = a.topk;
   int32_t *out = a.out_ids + ((int64_t)h * T + t) * k;
 
@@ -437,6 +438,9 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(IndexerArgs a) {
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
   }
+  // (every lane holds the same reductions; read as wave-uniform values they
+  // turn the search below into a scalar loop with more scalar instructions
+  // per step than the masked vector loop: 86 us against 77 us at 32k)
   const uint32_t diff = kmin ^ kmax;
   const int top = diff ? 31 - __clz(diff) : -1;
   uint32_t thr = top >= 31 ? 0u : (kmax >> (top + 1)) << (top + 1);
@@ -549,8 +553,7 @@ int launch_indexer(const IndexerArgs &a, hipStream_t stream) {
   }
   int st = check_launch("indexer_topk (score)");
   if (st) return st;
-  const int64_t rows = (int64_t)H * a.total_q;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)((a.total_q + 3) / 4), (unsigned)H);
   if (a.max_blocks <= 256) {
     hipLaunchKernelGGL(indexer_select_kernel<4>, grid, dim3(256), 0, stream, a);
   } else if (a.max_blocks <= 1024) {
