@@ -661,6 +661,27 @@ def test_token_mode_long_lists_unpipelined(gpu):
     assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "long lists")
 
 
+def test_token_mode_lists_past_the_latent_kernel_lds(gpu):
+    """V taken from K, 4096 ids per token and 256 tokens (nothing split): the
+    latent-row kernel's two 128-key K tiles leave LDS for 3584 ids, so the
+    call takes the 128-head kernel with staged V^T tiles instead."""
+    rng = np.random.default_rng(71)
+    T, Hq, S, topk = 256, 128, 9000, 4096
+    q8 = rand_codes(rng, (T, Hq, 576), 2.0)
+    kv8 = rand_codes(rng, (S, 576))
+    idx = np.stack([rng.permutation(S)[:topk] for _ in range(T)]).astype(np.int32)
+    idx[1, ::5] = -1
+    tl = np.full(T, topk, np.int32)
+    tl[2], tl[3] = 3, 3600
+    sk = (rng.standard_normal(Hq) * 3).astype(np.float32)
+    got = run_token(gpu, q8, kv8, idx, 1 / 24, k_scale=1.2, attn_sink=sk, topk_length=tl)
+    toks = np.array([0, 1, 2, 3, 77, 255])
+    ref = OA.sparse_attn_token(q8, kv8, idx, sm_scale=1 / 24, d_v=512, k_scale=1.2, attn_sink=sk,
+                               topk_length=tl, tokens=toks)
+    out, ml, lse = got
+    assert_attention_close((out[toks], ml[toks], lse[toks]), ref, "lists past the latent kernel's LDS")
+
+
 def test_token_mode_cache_past_2gb(gpu):
     """A 2.2 GB KV array (3.8M rows of 576 bytes): byte offsets outside the
     pipelined kernel's 32-bit range send 128-head groups to the gather kernel
