@@ -14,9 +14,10 @@
 // tile.  Only the K rows are staged: buffer-to-LDS DMA puts each tile's rows
 // in QK operand order, and the PV operands are read out of the same bytes.
 //  * S^T = K Q^T + C on 16x16x128 e4m3 MFMA (+ two 16x16x32 for the last
-//    64 bytes); C holds minus the row's reference maximum.
-//  * P = exp2(ck S - e) with one power-of-two exponent e per row and tile
-//    (the tile's row maximum lands in [2^7, 2^8)), split into two e4m3 codes,
+//    64 bytes), one 64-key half of the tile at a time; C holds minus the
+//    row's reference maximum.
+//  * P = exp2(ck S - e) with one power-of-two exponent e per row and half
+//    (the half's row maximum lands in [2^7, 2^8)), split into two e4m3 codes,
 //    hi = e4m3(P) and lo = e4m3(P - hi).  hi + lo carries P to about 2^-8
 //    relative, finer than a bf16 P.
 //  * O^T += V^T (hi + lo)^T as two scaled 16x16x128 e4m3 MFMAs sharing one
