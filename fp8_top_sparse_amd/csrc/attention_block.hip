@@ -76,16 +76,17 @@ struct Cfg {
   static_assert(kCols * 16 * WAVES == ROWS, "tile");
   static_assert(kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "staging");
 };
-// prefill: 256-row tiles, 8 waves of 32 rows (each K or V^T operand read
-// feeds two MFMAs), double-buffered
+// prefill with tiles converted in the kernel (short prompts): 256-row tiles,
+// 8 waves of 32 rows (each K or V^T operand read feeds two MFMAs),
+// double-buffered
 using PrefillCfg = Cfg<8, 256, 2>;
-using PrefillPreCfg = Cfg<8, 256, 2, true>;
-// the same 256-row tile as 16 waves of 16 rows, for prompts whose rows select
-// only part of their causal blocks: a wave skips every block that none of
-// its 16 rows selected, which happens more often than for 32 rows (32k
-// prompt, top-64: 3.164 ms against 3.23 ms; a prompt whose rows select every
-// causal block, as at 8k, runs 5% slower on it)
-using PrefillPreSparseCfg = Cfg<16, 256, 2, true>;
+// prefill from the pre-converted V^T pages: the same 256-row tile as 16 waves
+// of 16 rows, four per SIMD.  A wave skips every block that none of its 16
+// rows selected.  Against 8 waves of 32 rows (with the block and thread
+// indices, votes and lane masks kept scalar in both): 32k top-64 prompt
+// 2.64-2.84 ms against 2.85-2.91 ms, and the 8k prompt, whose rows select
+// every causal block, 0.236-0.241 ms against 0.250-0.254 ms.
+using PrefillPreCfg = Cfg<16, 256, 2, true>;
 // decode: few rows per kv head, so small single-buffered workgroups that
 // share a CU keep more pages in flight
 using DecodeCfg = Cfg<4, 64, 1>;
@@ -573,9 +574,6 @@ int launch_block_prefill(const AttnArgs &a, const Grid &gr, int64_t nblocks, hip
   const int64_t slots = (int64_t)a.batch * a.max_blocks * a.hkv;
   hipLaunchKernelGGL(vt_pages_kernel, dim3((unsigned)slots), dim3(256), 0, stream, a, gr.vt_pages);
   if (int st = check_launch("sparse_attn_fwd (V^T pages)")) return st;
-  // later rows of the longest prompt see more causal blocks than they select
-  if ((int64_t)a.topk * kPage < a.max_q_len)
-    return launch_block<PrefillPreSparseCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
   return launch_block<PrefillPreCfg>(a, gr, nblocks, stream, "sparse_attn_fwd (block prefill)");
 }
 
