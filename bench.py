@@ -114,6 +114,43 @@ def block_attention_flops(ids: np.ndarray, pos: np.ndarray, hq: int, hidx: int, 
     return keys * (hq // hidx) * 2 * (d_qk + d_v)
 
 
+def block_prefill_issued_flops(ids: np.ndarray, cu_seqlens_q, pos: np.ndarray, hq: int, hkv: int, hidx: int,
+                               d: int, max_blocks: int, rows_per_wg: int = 256):
+    """Matrix-core work the block prefill kernel issues for these selections
+    (QK + PV, 2 * 2 * d flop per row and key), as against the algorithmic
+    count: a workgroup takes rows_per_wg rows of one (sequence, kv head),
+    rows ordered token-major (row r: token r // G, head r % G), and visits the
+    union of its rows' selected blocks; each 16-row wave computes a block's
+    128 keys for all its rows when any of its rows selected the block, and
+    skips it otherwise.  None when G does not divide 16 (no such shapes here)."""
+    G = hq // hkv
+    gqi = hq // hidx
+    if 16 % G:
+        return None
+    tw, tt = 16 // G, rows_per_wg // G           # tokens per wave, per workgroup
+    T = ids.shape[1]
+    sel = np.zeros((hidx, T, max_blocks), bool)
+    for h in range(hidx):
+        r = np.repeat(np.arange(T), ids.shape[2])
+        v = ids[h].reshape(-1).astype(np.int64)
+        ok = (v >= 0) & (v < max_blocks)
+        sel[h, r[ok], v[ok]] = True
+    sel &= np.arange(max_blocks)[None, None, :] <= (pos // PAGE)[None, :, None]   # blocks with a visible key
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    waves = 0
+    for kh in range(hkv):
+        lists = sorted({(kh * G + h) // gqi for h in range(G)})
+        s_kh = np.logical_or.reduce(sel[lists], axis=0)          # [T, blocks]: any list of the token
+        for b in range(len(cu) - 1):
+            for t0 in range(int(cu[b]), int(cu[b + 1]), tt):
+                tile = s_kh[t0:min(t0 + tt, int(cu[b + 1]))]
+                union = tile.any(0)
+                pad = np.zeros((tt - tile.shape[0], max_blocks), bool)
+                per_wave = np.concatenate([tile, pad]).reshape(tt // tw, tw, max_blocks).any(1)
+                waves += int(per_wave[:, union].sum())
+    return waves * 16 * PAGE * d * 4
+
+
 def decode_attention_bytes(ids: np.ndarray, seq: np.ndarray, hq: int, hidx: int, hkv: int, d: int) -> int:
     """Algorithmic HBM bytes of block-mode decode attention: every (sequence, kv
     head) reads the K and V pages of the union of its index heads' selected
@@ -481,6 +518,12 @@ def run_workload(n: int, steps: int, warmup: int, producers: bool) -> dict:
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
                      "traffic": committed_traffic(n)},
     }
+    if block and wl.max_q_len > 1:
+        issued = block_prefill_issued_flops(ids_h, wl.cu_seqlens_q, pos, Hq, Hkv, Hidx, D, wl.block_table.shape[1])
+        if issued:
+            itf = issued / (ms["attn"] * 1e-3) / 1e12
+            res["attention_issued"] = {"gflop": round(issued / 1e9, 3), "useful_fraction": round(flops / issued, 4),
+                                       "tflops": round(itf, 3), "frac_fp8_peak": round(itf / PEAK_FP8_TFLOPS, 4)}
     if block:
         gbps = index_bytes / (ms["index"] * 1e-3) / 1e9
         res["indexer_topk_GBps"] = round(gbps, 1)
